@@ -1,0 +1,278 @@
+"""Plain fp64 CPU oracle: batch decode attention over a paged KV cache.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring). Slow on purpose: every
+request is gathered page by page into dense K/V and attended with a dense
+softmax in float64. No blocking, fusion or reordering beyond what the
+definition states.
+
+What is computed, and where the pages define it ("FlashInfer attention
+kernels" page, section flashinfer.decode › BatchDecodeWithPagedKVCacheWrapper,
+unless stated otherwise):
+
+* Page table (plan() parameters indptr / indices / last_page_len, and the
+  class example's comment that 1 <= last_page_len <= page_size): request i owns
+  pages indices[indptr[i]:indptr[i+1]]; every page but the last is full.
+* Sequence length: kv_len = page_size*(indptr[i+1]-indptr[i]-1) +
+  last_page_len[i] (the kv_len expression in the custom-mask part of the
+  BatchPrefillWithPagedKVCacheWrapper example on the same page).
+* Cache layouts (run() parameter paged_kv_cache): NHD pages are
+  [page_size, num_kv_heads, head_dim], HND pages are
+  [num_kv_heads, page_size, head_dim]; the 5-D form stacks K at index 0 and V
+  at index 1 of dimension 1.
+* Grouped heads (plan() notes): num_qo_heads is a multiple of num_kv_heads.
+  Reading taken: q head hq uses kv head hq // (num_qo_heads // num_kv_heads).
+* Logits: x = sm_scale * q.k (sm_scale default 1/sqrt(head_dim), stated in the
+  prefill plan() parameters); q_scale / k_scale / v_scale are the calibration
+  scales of run(), applied to q, K and V.
+* Soft cap (plan() parameter logits_soft_cap): if cap > 0 the logit x is
+  replaced by cap * tanh(x / cap). Reading taken: x is the scaled logit.
+* Window (plan() parameter window_left): a left window that includes its
+  edge; -1 means the whole sequence. Reading taken: the single query sits at
+  position kv_len-1 (the causal diagonal kv_len - qo_len of the prefill mask
+  example with qo_len = 1), so it sees tokens t >= kv_len-1-window_left.
+* Output (run() returns): o [batch, num_qo_heads, head_dim] and, on request,
+  lse [batch, num_qo_heads], the log-sum-exp of the final logits. Reading
+  taken: natural logarithm.
+* Split-KV (plan() parameter fixed_split_size, "in pages"): the sequence is
+  cut into chunks of that many pages; per-chunk states are combined by a
+  log-sum-exp merge (the merge_states step named there).
+"""
+import math
+
+import numpy as np
+
+from .fp8 import e4m3_to_f64
+
+DTYPES = ("f16", "bf16", "e4m3", "f32", "f64")
+
+
+def widen(a, dtype: str, scale: float = 1.0) -> np.ndarray:
+    """Exact float64 values of stored data, times a calibration scale.
+
+    ``f16`` arrays are np.float16; ``bf16`` arrays are the raw uint16 bit
+    patterns (numpy has no bfloat16); ``e4m3`` arrays are uint8 codes.
+    """
+    a = np.asarray(a)
+    if dtype == "f16":
+        if a.dtype != np.float16:
+            raise TypeError("f16 data must be np.float16")
+        out = a.astype(np.float64)
+    elif dtype == "bf16":
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 data must be raw np.uint16 bit patterns")
+        with np.errstate(invalid="ignore"):
+            out = (a.astype(np.uint32) << 16).view(np.float32).astype(
+                np.float64)
+    elif dtype == "e4m3":
+        out = e4m3_to_f64(a)
+    elif dtype in ("f32", "f64"):
+        out = a.astype(np.float64)
+    else:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    return out * float(scale) if scale != 1.0 else out
+
+
+def kv_lengths(indptr, last_page_len, page_size: int) -> np.ndarray:
+    """Per-request KV length from the CSR page table."""
+    indptr = np.asarray(indptr, dtype=np.int64)
+    last = np.asarray(last_page_len, dtype=np.int64)
+    npages = indptr[1:] - indptr[:-1]
+    if np.any(npages < 1):
+        raise ValueError("every request needs at least one page")
+    if np.any(last < 1) or np.any(last > page_size):
+        raise ValueError("last_page_len must lie in [1, page_size]")
+    return page_size * (npages - 1) + last
+
+
+def window_start(kv_len: int, window_left: int) -> int:
+    """First attended token of a request whose query sits at kv_len-1."""
+    if window_left < 0:
+        return 0
+    return max(0, kv_len - 1 - window_left)
+
+
+def gather_request(k_cache, v_cache, layout: str, indices, indptr, i: int,
+                   kv_len: int, page_size: int):
+    """Dense K and V [kv_len, num_kv_heads, head_dim] of request i, bit-exact.
+
+    ``k_cache`` / ``v_cache`` are the 4-D per-tensor caches (for the 5-D form
+    pass cache[:, 0] and cache[:, 1]). The stored dtype is kept unchanged.
+    """
+    t = np.arange(kv_len)
+    pages = np.asarray(indices)[int(indptr[i]) + t // page_size]
+    slots = t % page_size
+    if layout == "NHD":
+        return k_cache[pages, slots], v_cache[pages, slots]
+    if layout == "HND":
+        # [page, head, slot, dim] -> pick (page, slot) per token, keep heads.
+        return (k_cache[pages, :, slots, :], v_cache[pages, :, slots, :])
+    raise ValueError(f"unknown layout {layout!r}")
+
+
+def attention_state(q, K, V, sm_scale: float, logits_soft_cap: float = 0.0,
+                    return_weights: bool = False):
+    """Dense softmax attention of one query row per q head over n tokens.
+
+    q: [num_qo_heads, head_dim]; K, V: [n, num_kv_heads, head_dim]; all fp64.
+    Returns (o [num_qo_heads, head_dim], lse [num_qo_heads]) and, if asked,
+    the weights p [num_qo_heads, n]. With n == 0 the state is empty:
+    o = 0, lse = -inf.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    nq, hd = q.shape
+    n, nkv, _ = K.shape
+    if nq % nkv:
+        raise ValueError("num_qo_heads must be a multiple of num_kv_heads")
+    group = nq // nkv
+    o = np.zeros((nq, hd))
+    lse = np.full(nq, -np.inf)
+    p_all = np.zeros((nq, n))
+    if n == 0:
+        return (o, lse, p_all) if return_weights else (o, lse)
+    for hq in range(nq):
+        h = hq // group
+        x = sm_scale * (K[:, h, :] @ q[hq])
+        if logits_soft_cap > 0:
+            x = logits_soft_cap * np.tanh(x / logits_soft_cap)
+        m = x.max()
+        p = np.exp(x - m)
+        z = p.sum()
+        o[hq] = (p @ V[:, h, :]) / z
+        lse[hq] = m + math.log(z)
+        p_all[hq] = p / z
+    return (o, lse, p_all) if return_weights else (o, lse)
+
+
+def _request_f64(q_i, K, V, q_dtype, kv_dtype, q_scale, k_scale, v_scale):
+    return (widen(q_i, q_dtype, q_scale), widen(K, kv_dtype, k_scale),
+            widen(V, kv_dtype, v_scale))
+
+
+def decode_request(q_i, K, V, q_dtype: str, kv_dtype: str, sm_scale: float,
+                   logits_soft_cap: float = 0.0, window_left: int = -1,
+                   q_scale: float = 1.0, k_scale: float = 1.0,
+                   v_scale: float = 1.0):
+    """Decode attention of one request from its gathered (stored-dtype) K/V."""
+    kv_len = K.shape[0]
+    s0 = window_start(kv_len, window_left)
+    qf, Kf, Vf = _request_f64(q_i, K[s0:], V[s0:], q_dtype, kv_dtype,
+                              q_scale, k_scale, v_scale)
+    return attention_state(qf, Kf, Vf, sm_scale, logits_soft_cap)
+
+
+def _cache_pair(paged_kv_cache):
+    if isinstance(paged_kv_cache, (tuple, list)):
+        return paged_kv_cache[0], paged_kv_cache[1]
+    return paged_kv_cache[:, 0], paged_kv_cache[:, 1]
+
+
+def batch_decode(q, paged_kv_cache, layout: str, indptr, indices,
+                 last_page_len, page_size: int, q_dtype: str, kv_dtype: str,
+                 sm_scale: float, logits_soft_cap: float = 0.0,
+                 window_left: int = -1, q_scale: float = 1.0,
+                 k_scale: float = 1.0, v_scale: float = 1.0, requests=None):
+    """o [len(requests), num_qo_heads, head_dim] and lse, both fp64.
+
+    ``q`` is [batch, num_qo_heads, head_dim] in its stored dtype;
+    ``paged_kv_cache`` is the 5-D cache or a (k_cache, v_cache) pair.
+    ``requests`` selects a subset of the batch (default: all).
+    """
+    k_cache, v_cache = _cache_pair(paged_kv_cache)
+    lens = kv_lengths(indptr, last_page_len, page_size)
+    reqs = range(len(lens)) if requests is None else list(requests)
+    nq, hd = q.shape[1], q.shape[2]
+    o = np.zeros((len(reqs), nq, hd))
+    lse = np.zeros((len(reqs), nq))
+    for r, i in enumerate(reqs):
+        K, V = gather_request(k_cache, v_cache, layout, indices, indptr, i,
+                              int(lens[i]), page_size)
+        o[r], lse[r] = decode_request(q[i], K, V, q_dtype, kv_dtype, sm_scale,
+                                      logits_soft_cap, window_left, q_scale,
+                                      k_scale, v_scale)
+    return o, lse
+
+
+def chunk_bounds(kv_len: int, page_size: int, split_pages: int,
+                 window_left: int = -1):
+    """Token ranges [begin, end) of the fixed-size chunks of one request.
+
+    Chunk c covers pages [c*split_pages, (c+1)*split_pages) counted from the
+    request's first page, cut to the attended range [window start, kv_len).
+    Chunks with nothing to attend are dropped. split_pages <= 0 means one
+    chunk.
+    """
+    s0 = window_start(kv_len, window_left)
+    if split_pages <= 0:
+        return [(s0, kv_len)]
+    step = split_pages * page_size
+    out = []
+    for b in range(0, kv_len, step):
+        lo, hi = max(b, s0), min(b + step, kv_len)
+        if lo < hi:
+            out.append((lo, hi))
+    return out
+
+
+def merge_states(v, s):
+    """Log-sum-exp merge of attention states, chunk by chunk.
+
+    v: [rows, n, head_dim] per-chunk normalised outputs; s: [rows, n] per-chunk
+    natural-log LSE. Returns (v_merged [rows, head_dim], s_merged [rows]).
+    A state with s = -inf is empty and contributes nothing; rows whose states
+    are all empty give v = 0, s = -inf.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)
+    rows, n, hd = v.shape
+    v_out = np.zeros((rows, hd))
+    s_out = np.full(rows, -np.inf)
+    for r in range(rows):
+        m = s[r].max() if n else -np.inf
+        if m == -np.inf:
+            continue
+        w = np.exp(s[r] - m)
+        z = w.sum()
+        v_out[r] = (w @ v[r]) / z
+        s_out[r] = m + math.log(z)
+    return v_out, s_out
+
+
+def decode_request_split(q_i, K, V, q_dtype: str, kv_dtype: str,
+                         sm_scale: float, page_size: int, split_pages: int,
+                         logits_soft_cap: float = 0.0, window_left: int = -1,
+                         q_scale: float = 1.0, k_scale: float = 1.0,
+                         v_scale: float = 1.0):
+    """Split-KV decode of one request: per-chunk states, then merge_states."""
+    kv_len = K.shape[0]
+    qf, Kf, Vf = _request_f64(q_i, K, V, q_dtype, kv_dtype, q_scale, k_scale,
+                              v_scale)
+    states = [attention_state(qf, Kf[a:b], Vf[a:b], sm_scale, logits_soft_cap)
+              for a, b in chunk_bounds(kv_len, page_size, split_pages,
+                                       window_left)]
+    v = np.stack([st[0] for st in states], axis=1)   # [nq, n, hd]
+    s = np.stack([st[1] for st in states], axis=1)   # [nq, n]
+    return merge_states(v, s)
+
+
+def batch_decode_split(q, paged_kv_cache, layout: str, indptr, indices,
+                       last_page_len, page_size: int, q_dtype: str,
+                       kv_dtype: str, sm_scale: float, split_pages: int,
+                       logits_soft_cap: float = 0.0, window_left: int = -1,
+                       q_scale: float = 1.0, k_scale: float = 1.0,
+                       v_scale: float = 1.0, requests=None):
+    """batch_decode through fixed-size chunks and merge_states."""
+    k_cache, v_cache = _cache_pair(paged_kv_cache)
+    lens = kv_lengths(indptr, last_page_len, page_size)
+    reqs = range(len(lens)) if requests is None else list(requests)
+    nq, hd = q.shape[1], q.shape[2]
+    o = np.zeros((len(reqs), nq, hd))
+    lse = np.zeros((len(reqs), nq))
+    for r, i in enumerate(reqs):
+        K, V = gather_request(k_cache, v_cache, layout, indices, indptr, i,
+                              int(lens[i]), page_size)
+        o[r], lse[r] = decode_request_split(
+            q[i], K, V, q_dtype, kv_dtype, sm_scale, page_size, split_pages,
+            logits_soft_cap, window_left, q_scale, k_scale, v_scale)
+    return o, lse

@@ -1,0 +1,1 @@
+"""Paged-KV batch decode attention for AMD MI355X (gfx950)."""

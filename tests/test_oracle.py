@@ -1,0 +1,404 @@
+"""Pins of the fp64 CPU oracle against facts fixed outside the oracle.
+
+Each test checks the oracle against something other than itself: the values
+the decode API page prints for its class example, a library routine
+(torch's scaled_dot_product_attention, torch's fp8/bf16 casts), brute force on
+tiny inputs, closed forms, or invariants of softmax attention. A plausible
+mistake (a wrong head mapping, an off-by-one length or window edge, a
+transposed layout, a wrong soft-cap order, a base-2 LSE) fails at least one.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import fp8 as ofp8
+from paged_kv_decode_09_amd import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- helpers
+
+def scatter_to_pages(K_list, V_list, layout, page_size, pool_pages, rng,
+                     fill=np.nan, dtype=np.float64):
+    """Independent writer: lay dense per-request K/V out in a paged cache.
+
+    Written with explicit loops over tokens, unlike the oracle's gather.
+    Returns (cache [pool, 2, ...], indptr, indices, last_page_len).
+    """
+    nkv, hd = K_list[0].shape[1], K_list[0].shape[2]
+    npages = [(len(K) + page_size - 1) // page_size for K in K_list]
+    used = sum(npages)
+    perm = rng.permutation(pool_pages)[:used]
+    if layout == "NHD":
+        cache = np.full((pool_pages, 2, page_size, nkv, hd), fill, dtype=dtype)
+    else:
+        cache = np.full((pool_pages, 2, nkv, page_size, hd), fill, dtype=dtype)
+    indptr = [0]
+    last = []
+    cursor = 0
+    for K, V, n in zip(K_list, V_list, npages):
+        for tok in range(len(K)):
+            page = perm[cursor + tok // page_size]
+            slot = tok % page_size
+            for h in range(nkv):
+                if layout == "NHD":
+                    cache[page, 0, slot, h, :] = K[tok, h]
+                    cache[page, 1, slot, h, :] = V[tok, h]
+                else:
+                    cache[page, 0, h, slot, :] = K[tok, h]
+                    cache[page, 1, h, slot, :] = V[tok, h]
+        cursor += n
+        indptr.append(cursor)
+        last.append(len(K) - page_size * (n - 1))
+    return (cache, np.array(indptr, np.int32), perm.astype(np.int32),
+            np.array(last, np.int32))
+
+
+def sdpa_decode(q, K, V, sm_scale, lo=0):
+    """torch SDPA (fp64, CPU) of one query row per head over tokens [lo, L).
+
+    Grouped heads are expanded by SDPA itself (enable_gqa)."""
+    qt = torch.from_numpy(np.ascontiguousarray(q))[None, :, None, :]
+    kt = torch.from_numpy(np.ascontiguousarray(K[lo:].transpose(1, 0, 2)))[None]
+    vt = torch.from_numpy(np.ascontiguousarray(V[lo:].transpose(1, 0, 2)))[None]
+    o = F.scaled_dot_product_attention(qt, kt, vt, scale=sm_scale,
+                                       enable_gqa=True)
+    return o[0, :, 0, :].numpy()
+
+
+def rand_case(rng, lengths, nq, nkv, hd):
+    K = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    V = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    q = rng.standard_normal((len(lengths), nq, hd))
+    return q, K, V
+
+
+# ---------------------------------------------------------- stored formats
+
+def test_e4m3_table_matches_torch_cast():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float32).double().numpy()
+    mine = ofp8.E4M3_TABLE
+    assert np.array_equal(np.isnan(ref), np.isnan(mine))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], mine[ok])
+    # signed zero is preserved too
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(mine[ok]))
+
+
+def test_e4m3_spot_values():
+    t = ofp8.E4M3_TABLE
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0       # largest finite
+    assert t[0x01] == 2.0 ** -9                          # smallest subnormal
+    assert t[0x07] == 7 * 2.0 ** -9                      # largest subnormal
+    assert t[0x08] == 2.0 ** -6                          # smallest normal
+    assert t[0x38] == 1.0 and t[0xB8] == -1.0
+    assert t[0x00] == 0.0 and np.signbit(t[0x80])
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert np.sum(np.isnan(t)) == 2                      # no inf, 2 NaNs
+
+
+def test_bf16_and_f16_widening_match_torch():
+    rng = np.random.default_rng(0)
+    bits = rng.integers(0, 1 << 16, 4096, dtype=np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    ref = ref.double().numpy()
+    mine = oracle.widen(bits, "bf16")
+    assert np.array_equal(np.isnan(ref), np.isnan(mine))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], mine[ok])
+    h = rng.standard_normal(1000).astype(np.float16)
+    assert np.array_equal(oracle.widen(h, "f16"),
+                          torch.from_numpy(h).double().numpy())
+    codes = np.arange(256, dtype=np.uint8)
+    sc = oracle.widen(codes, "e4m3", 1.0 / 64)
+    ok = ~np.isnan(sc)
+    assert np.array_equal(sc[ok], ofp8.E4M3_TABLE[ok] / 64)
+
+
+# ------------------------------------------------- the pages' worked example
+
+def test_worked_example_lengths_and_shape():
+    g = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    lens = oracle.kv_lengths(g["kv_page_indptr"], g["kv_last_page_len"],
+                             g["page_size"])
+    assert lens.tolist() == g["kv_len_by_hand"]
+    w = wl.WORKLOADS["worked_example"]
+    case = wl.make_case(w)
+    assert list(case.pool.shape) == g["cache_shape_per_layer"]
+    assert case.pt.indptr.tolist() == g["kv_page_indptr"]
+    assert case.pt.last_page_len.tolist() == g["kv_last_page_len"]
+    assert case.pt.indices.tolist() == list(range(g["max_num_pages"]))
+    assert case.pt.lengths.tolist() == g["kv_len_by_hand"]
+    pool = wl.raw_numpy(case.pool, "f16")
+    o, lse = oracle.batch_decode(
+        wl.raw_numpy(case.q, "f16"), pool, "NHD", case.pt.indptr,
+        case.pt.indices, case.pt.last_page_len, 16, "f16", "f16", w.sm_scale)
+    assert list(o.shape) == g["printed_output_shape"]
+    assert lse.shape == (g["batch_size"], g["num_qo_heads"])
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+def test_generator_lengths_round_trip_through_kv_len():
+    """The generator writes a page table from drawn lengths; the oracle's
+    kv_len must read the same lengths back (independent writer/reader)."""
+    rng = np.random.default_rng(3)
+    for ps in (1, 2, 4, 16, 64):
+        lens = rng.integers(1, 500, 40)
+        pt = wl.page_table_for(lens, ps, "perm_used", rng)
+        assert np.array_equal(
+            oracle.kv_lengths(pt.indptr, pt.last_page_len, ps), lens)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(indptr=[0, 0, 3], last=[1, 1]),     # empty request
+    dict(indptr=[0, 2, 3], last=[0, 1]),     # last_page_len 0
+    dict(indptr=[0, 2, 3], last=[17, 1]),    # last_page_len > page_size
+])
+def test_kv_len_rejects_invalid_tables(bad):
+    with pytest.raises(ValueError):
+        oracle.kv_lengths(bad["indptr"], bad["last"], 16)
+
+
+# ------------------------------------------------------------------ gather
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+@pytest.mark.parametrize("page_size", [1, 2, 4, 16])
+def test_gather_returns_written_rows_bit_exactly(layout, page_size):
+    rng = np.random.default_rng(page_size + (layout == "HND") * 100)
+    lengths = [1, page_size, page_size + 1, 37, 3 * page_size]
+    _, K, V = rand_case(rng, lengths, 4, 2, 8)
+    npages = sum((L + page_size - 1) // page_size for L in lengths)
+    cache, indptr, indices, last = scatter_to_pages(
+        K, V, layout, page_size, npages + 7, rng)
+    lens = oracle.kv_lengths(indptr, last, page_size)
+    assert lens.tolist() == lengths
+    for i, L in enumerate(lengths):
+        Kg, Vg = oracle.gather_request(cache[:, 0], cache[:, 1], layout,
+                                       indices, indptr, i, int(lens[i]),
+                                       page_size)
+        assert Kg.shape == K[i].shape
+        assert np.array_equal(Kg, K[i]) and np.array_equal(Vg, V[i])
+        assert not np.isnan(Kg).any()   # unused slots (NaN) never gathered
+
+
+# ------------------------------------------------- attention vs a library
+
+@pytest.mark.parametrize("group", [1, 2, 4])
+@pytest.mark.parametrize("page_size", [1, 2, 4, 16])
+@pytest.mark.parametrize("hd", [4, 8])
+def test_decode_matches_torch_sdpa(group, page_size, hd):
+    rng = np.random.default_rng(group * 100 + page_size * 10 + hd)
+    nkv = 2
+    nq = nkv * group
+    lengths = list(rng.integers(1, 41, 3))
+    q, K, V = rand_case(rng, lengths, nq, nkv, hd)
+    npages = sum((L + page_size - 1) // page_size for L in lengths)
+    for layout in ("NHD", "HND"):
+        cache, indptr, indices, last = scatter_to_pages(
+            K, V, layout, page_size, npages + 3, rng)
+        sm = 1.0 / math.sqrt(hd)
+        o, lse = oracle.batch_decode(q, cache, layout, indptr, indices,
+                                     last, page_size, "f64", "f64", sm)
+        for i in range(len(lengths)):
+            ref = sdpa_decode(q[i], K[i], V[i], sm)
+            assert np.max(np.abs(o[i] - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("window", [0, 1, 5, 17, 39, 1000])
+def test_window_matches_sdpa_on_the_last_tokens(window):
+    rng = np.random.default_rng(window + 11)
+    lengths = [40, 17, 1, 6]
+    q, K, V = rand_case(rng, lengths, 4, 2, 8)
+    cache, indptr, indices, last = scatter_to_pages(K, V, "NHD", 4, 40, rng)
+    sm = 0.3
+    o, _ = oracle.batch_decode(q, cache, "NHD", indptr, indices, last, 4,
+                               "f64", "f64", sm, window_left=window)
+    for i, L in enumerate(lengths):
+        n_attended = min(L, window + 1)   # inclusive left window
+        ref = sdpa_decode(q[i], K[i], V[i], sm, lo=L - n_attended)
+        assert np.max(np.abs(o[i] - ref)) < 1e-12
+
+
+# ----------------------------------------------------- closed forms/special
+
+def test_softmax_weights_sum_to_one():
+    rng = np.random.default_rng(5)
+    q, K, V = rand_case(rng, [33], 8, 2, 16)
+    _, _, p = oracle.attention_state(q[0], K[0], V[0], 0.25,
+                                     return_weights=True)
+    assert np.all(p >= 0)
+    assert np.max(np.abs(p.sum(axis=1) - 1.0)) < 1e-12
+
+
+@pytest.mark.parametrize("window", [-1, 0, 3, 50, 499])
+def test_zero_query_gives_log_count_and_mean(window):
+    """q = 0 makes every logit 0: lse = ln(#attended), o = mean of V."""
+    rng = np.random.default_rng(9)
+    lengths = [500, 64, 1, 129]
+    _, K, V = rand_case(rng, lengths, 4, 2, 8)
+    q = np.zeros((len(lengths), 4, 8))
+    cache, indptr, indices, last = scatter_to_pages(K, V, "HND", 16, 60, rng)
+    o, lse = oracle.batch_decode(q, cache, "HND", indptr, indices, last, 16,
+                                 "f64", "f64", 0.5, window_left=window)
+    for i, L in enumerate(lengths):
+        n = L if window < 0 else min(L, window + 1)
+        assert np.all(np.abs(lse[i] - math.log(n)) < 1e-12)
+        mean = V[i][L - n:].mean(axis=0)            # [nkv, hd]
+        ref = np.repeat(mean, 2, axis=0)            # heads hq -> hq // 2
+        assert np.max(np.abs(o[i] - ref)) < 1e-12
+
+
+def test_constant_keys_give_closed_form_lse():
+    """All keys equal k: every logit is sm*q.k, so lse = sm*q.k + ln(n)."""
+    rng = np.random.default_rng(12)
+    L, nkv, hd = 77, 2, 8
+    k = rng.standard_normal((nkv, hd))
+    K = np.broadcast_to(k, (L, nkv, hd)).copy()
+    V = rng.standard_normal((L, nkv, hd))
+    q = rng.standard_normal((4, hd))
+    o, lse = oracle.attention_state(q, K, V, 0.7)
+    for hq in range(4):
+        h = hq // 2
+        assert abs(lse[hq] - (0.7 * float(np.dot(q[hq], k[h])) + math.log(L))) < 1e-12
+        assert np.max(np.abs(o[hq] - V[:, h].mean(axis=0))) < 1e-12
+
+
+def test_window_zero_returns_last_value_exactly():
+    rng = np.random.default_rng(13)
+    lengths = [1, 2, 19, 64]
+    q, K, V = rand_case(rng, lengths, 6, 3, 8)
+    cache, indptr, indices, last = scatter_to_pages(K, V, "NHD", 16, 10, rng)
+    o, lse = oracle.batch_decode(q, cache, "NHD", indptr, indices, last, 16,
+                                 "f64", "f64", 1.0, window_left=0)
+    for i, L in enumerate(lengths):
+        assert np.array_equal(o[i], np.repeat(V[i][L - 1], 2, axis=0))
+
+
+def test_soft_cap_huge_equals_uncapped():
+    rng = np.random.default_rng(14)
+    q, K, V = rand_case(rng, [50], 4, 2, 8)
+    a = oracle.attention_state(q[0], K[0], V[0], 0.35)
+    b = oracle.attention_state(q[0], K[0], V[0], 0.35, logits_soft_cap=1e9)
+    assert np.max(np.abs(a[0] - b[0])) < 1e-9
+    assert np.max(np.abs(a[1] - b[1])) < 1e-9
+
+
+def test_soft_cap_saturates_to_plus_minus_cap():
+    """Logits of magnitude >> cap saturate to +-cap: the positive-logit tokens
+    share the weight equally and lse = cap + ln(#positive)."""
+    rng = np.random.default_rng(15)
+    L, hd, cap = 40, 4, 50.0
+    sign = np.where(rng.random(L) < 0.4, 1.0, -1.0)
+    K = np.zeros((L, 1, hd))
+    K[:, 0, 0] = sign * (1.0 + rng.random(L))
+    K[:, 0, 1:] = rng.standard_normal((L, hd - 1))
+    V = rng.standard_normal((L, 1, hd))
+    q = np.zeros((1, hd))
+    q[0, 0] = 1e4                       # |x| >= 0.5 * 1e4 >> cap
+    o, lse = oracle.attention_state(q, K, V, 0.5, logits_soft_cap=cap)
+    pos = sign > 0
+    assert abs(lse[0] - (cap + math.log(pos.sum()))) < 1e-9
+    assert np.max(np.abs(o[0] - V[pos, 0].mean(axis=0))) < 1e-12
+
+
+def test_soft_cap_bounds_every_logit():
+    rng = np.random.default_rng(16)
+    L, cap = 64, 3.0
+    q, K, V = rand_case(rng, [L], 2, 1, 8)
+    q *= 20.0
+    _, lse = oracle.attention_state(q[0], K[0], V[0], 1.0,
+                                    logits_soft_cap=cap)
+    assert np.all(lse < cap + math.log(L)) and np.all(lse > -cap + math.log(L))
+
+
+# ------------------------------------------------------------ split + merge
+
+@pytest.mark.parametrize("split_pages", [1, 2, 3, 8, 64])
+@pytest.mark.parametrize("window", [-1, 0, 37, 200])
+def test_split_then_merge_equals_unsplit(split_pages, window):
+    rng = np.random.default_rng(split_pages * 7 + window)
+    lengths = [1, 16, 17, 250, 129]
+    q, K, V = rand_case(rng, lengths, 8, 2, 8)
+    cache, indptr, indices, last = scatter_to_pages(K, V, "NHD", 16, 40, rng)
+    args = (q, cache, "NHD", indptr, indices, last, 16, "f64", "f64", 0.4)
+    o1, l1 = oracle.batch_decode(*args, window_left=window)
+    o2, l2 = oracle.batch_decode_split(*args, split_pages, window_left=window)
+    assert np.max(np.abs(o1 - o2)) < 1e-12
+    assert np.max(np.abs(l1 - l2)) < 1e-12
+
+
+def test_merge_states_of_disjoint_parts_matches_sdpa_on_union():
+    rng = np.random.default_rng(21)
+    L, nkv, hd = 90, 2, 8
+    q, K, V = rand_case(rng, [L], 4, nkv, hd)
+    cuts = [0, 13, 14, 60, 90]
+    parts = [oracle.attention_state(q[0], K[0][a:b], V[0][a:b], 0.3)
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    v = np.stack([p[0] for p in parts], axis=1)
+    s = np.stack([p[1] for p in parts], axis=1)
+    o, _ = oracle.merge_states(v, s)
+    ref = sdpa_decode(q[0], K[0], V[0], 0.3)
+    assert np.max(np.abs(o - ref)) < 1e-12
+
+
+def test_merge_states_empty_states():
+    v = np.ones((3, 2, 4))
+    s = np.array([[-np.inf, -np.inf], [-np.inf, 0.5], [1.0, 1.0]])
+    vo, so = oracle.merge_states(v * np.array([1.0, 2.0])[None, :, None], s)
+    assert np.all(vo[0] == 0) and so[0] == -np.inf
+    assert np.allclose(vo[1], 2.0) and so[1] == 0.5
+    assert np.allclose(vo[2], 1.5) and abs(so[2] - (1.0 + math.log(2))) < 1e-15
+
+
+def test_chunk_bounds_cover_the_attended_range():
+    for L in (1, 15, 16, 17, 255, 256, 257, 4096, 5000):
+        for S in (1, 2, 5, 16):
+            for w in (-1, 0, 10, 300):
+                ch = oracle.chunk_bounds(L, 16, S, w)
+                s0 = oracle.window_start(L, w)
+                assert ch[0][0] == s0 and ch[-1][1] == L
+                for (a, b), (c, _) in zip(ch[:-1], ch[1:]):
+                    assert b == c and b % (16 * S) == 0
+                for a, b in ch:
+                    assert 0 < b - a <= 16 * S
+
+
+# ------------------------------------------- inputs used by the GPU parity
+
+@pytest.mark.parametrize("name", ["worked_example", "serving_batch",
+                                  "long_context", "gemma2_decode", "fp8_kv"])
+def test_named_workload_page_tables(name):
+    w = wl.WORKLOADS[name]
+    rng = np.random.default_rng(w.seed)
+    pt = wl.make_page_table(w, rng)
+    assert len(pt.lengths) == w.batch
+    assert np.array_equal(oracle.kv_lengths(pt.indptr, pt.last_page_len,
+                                            w.page_size), pt.lengths)
+    # every page used once, inside the pool
+    assert len(np.unique(pt.indices)) == len(pt.indices)
+    assert pt.indices.min() >= 0 and pt.indices.max() < pt.pool_pages
+
+
+def test_poison_fills_only_unreadable_slots():
+    w = wl.small_workload(batch=4, lengths=("uniform", 1, 60), pool_pages=30)
+    case = wl.make_case(w, poison=True)
+    pool = wl.raw_numpy(case.pool, "f16").astype(np.float64)
+    lens = oracle.kv_lengths(case.pt.indptr, case.pt.last_page_len, 16)
+    seen = 0
+    for i, L in enumerate(lens):
+        K, V = oracle.gather_request(pool[:, 0], pool[:, 1], "NHD",
+                                     case.pt.indices, case.pt.indptr, i,
+                                     int(L), 16)
+        assert not np.isnan(K).any() and not np.isnan(V).any()
+        seen += int(L)
+    # everything not gathered is NaN
+    total = pool[:, 0, :, 0, 0].size
+    assert np.isnan(pool[:, 0, :, 0, 0]).sum() == total - seen
