@@ -1,0 +1,200 @@
+/*
+ * pkd.h - paged-KV batch decode attention on AMD MI355X (gfx950, CDNA4).
+ *
+ * The operation is the one of flashinfer.decode.BatchDecodeWithPagedKVCacheWrapper
+ * on the "FlashInfer attention kernels" API page: every request of a batch has
+ * ONE query token per q head, and it attends the keys/values stored in that
+ * request's pages of a paged KV cache. Pages are found through a CSR page
+ * table (indptr / indices / last_page_len). q heads are grouped onto kv heads
+ * (grouped-query attention). Options: sm_scale, logits_soft_cap, window_left,
+ * fixed_split_size / disable_split_kv, fp8 E4M3 keys/values with calibration
+ * scales. A long sequence may be cut into chunks whose partial states are
+ * combined by a log-sum-exp merge (the merge_states step named on that page).
+ *
+ * Definitions used throughout (same page and section):
+ *   B        batch size; request i owns pages indices[indptr[i] .. indptr[i+1])
+ *   P        page_size; 1 <= last_page_len[i] <= P (class example comment)
+ *   L_i      kv_len = P*(indptr[i+1]-indptr[i]-1) + last_page_len[i]
+ *            (kv_len expression of the prefill wrapper's custom-mask example)
+ *   G        num_qo_heads / num_kv_heads; q head hq reads kv head hq / G
+ *   window   window_left >= 0 keeps tokens t >= L_i-1-window_left (inclusive
+ *            left window; the query sits at position L_i-1); -1 keeps all
+ *   logits   x = sm_scale*q_scale*k_scale * (q . k); if logits_soft_cap > 0,
+ *            x <- cap*tanh(x/cap)
+ *   o        sum_t softmax(x)_t * v_scale * v_t ;  lse = ln sum_t exp(x_t)
+ *
+ * Memory and streams.
+ *   Every device buffer (q, caches, indices, o, lse, workspace) is owned by
+ *   the caller. `stream` arguments are hipStream_t values passed as void*
+ *   (NULL = the default stream). pkd_run* only enqueue work on `stream`: they
+ *   never allocate, never synchronise and never read device memory on the
+ *   host.
+ *
+ * Errors.
+ *   Every call returns a pkd_status; on failure pkd_last_error() returns a
+ *   thread-local message that names the offending value and the limit.
+ *   Nothing is launched when a call fails.
+ */
+#ifndef PKD_H_
+#define PKD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKD_ABI_VERSION 1
+
+typedef enum {
+  PKD_OK = 0,
+  PKD_EINVAL = -1,        /* invalid argument or page table               */
+  PKD_EUNSUPPORTED = -2,  /* valid, but not built (head_dim, dtype, ...)  */
+  PKD_EHIP = -3,          /* a HIP runtime call failed                    */
+  PKD_ENOMEM = -4,        /* host or device allocation failed (plan only) */
+  PKD_EWORKSPACE = -5     /* workspace missing or smaller than required   */
+} pkd_status;
+
+/* Stored element types. E4M3 is the OCP fp8 "fn" format (torch.float8_e4m3fn):
+ * bias 7, no infinities, NaN = 0x7F/0xFF, largest finite 448. */
+typedef enum { PKD_F16 = 0, PKD_BF16 = 1, PKD_E4M3 = 2, PKD_F32 = 3 } pkd_dtype;
+
+/* Cache layouts of the run() parameter paged_kv_cache:
+ *   NHD: one page of K (or V) is [P][num_kv_heads][head_dim]
+ *   HND: one page of K (or V) is [num_kv_heads][P][head_dim]
+ * head_dim is always contiguous. */
+typedef enum { PKD_NHD = 0, PKD_HND = 1 } pkd_layout;
+
+/* Problem description of plan(). Enum-valued fields are int32_t (values from
+ * the enums above) so that the struct layout is fixed. */
+typedef struct {
+  int32_t batch_size;       /* B >= 0                                       */
+  int32_t num_qo_heads;     /* >= 1, a multiple of num_kv_heads             */
+  int32_t num_kv_heads;     /* >= 1; G = num_qo_heads/num_kv_heads <= 16    */
+  int32_t head_dim;         /* 64, 128 or 256                               */
+  int32_t page_size;        /* a power of two, 1 .. 256                     */
+  int32_t layout;           /* pkd_layout                                   */
+  int32_t q_dtype;          /* PKD_F16 or PKD_BF16                          */
+  int32_t kv_dtype;         /* q_dtype or PKD_E4M3                          */
+  int32_t o_dtype;          /* PKD_F16 or PKD_BF16                          */
+  float sm_scale;           /* finite; 1/sqrt(head_dim) is the usual value  */
+  float logits_soft_cap;    /* <= 0: off; else cap*tanh(x/cap)              */
+  int32_t window_left;      /* -1: whole sequence; >= 0: inclusive window   */
+  int32_t fixed_split_size; /* pages per chunk; 0: the planner chooses      */
+  int32_t disable_split_kv; /* nonzero: exactly one chunk per request       */
+} pkd_plan_params;
+
+/* One unit of decode work: the tokens [token_begin, token_end) of one chunk of
+ * one request, for one kv head and its G q heads. */
+typedef struct {
+  int32_t request;
+  int32_t kv_head;
+  int32_t token_begin;      /* first attended token of the chunk            */
+  int32_t token_end;        /* one past the last attended token             */
+  int32_t page_base;        /* indptr[request]                              */
+  int32_t partial;          /* -1: writes o/lse; else its workspace slot    */
+  int32_t chunk;            /* chunk index within the request (ascending)   */
+  int32_t reserved;
+} pkd_work_item;
+
+typedef struct {
+  int32_t num_items;        /* work items = decode workgroups               */
+  int32_t num_split_requests; /* requests cut into more than one chunk      */
+  int32_t num_partials;     /* workspace slots (chunks of split requests)   */
+  int32_t split_pages;      /* chunk size in pages; 0 = no split            */
+  int64_t attended_tokens;  /* sum over requests of attended tokens         */
+  size_t workspace_bytes;   /* bytes the workspace of pkd_run must hold     */
+} pkd_plan_info;
+
+typedef struct pkd_plan pkd_plan; /* opaque, owned by the library */
+
+int32_t pkd_abi_version(void);
+
+/* Message of the last failed call on this thread ("" if none). The pointer
+ * stays valid until the next pkd_* call on the same thread. */
+const char* pkd_last_error(void);
+
+/* plan(): validate the page table, choose the chunking and build the work
+ * list (flashinfer.decode › BatchDecodeWithPagedKVCacheWrapper › plan()).
+ *   indptr         host, int32 [B+1], read during the call only
+ *   last_page_len  host, int32 [B],   read during the call only
+ *   indices        DEVICE, int32 [indptr[B]], BORROWED: it must stay alive and
+ *                  unchanged while the plan is used; every entry must index a
+ *                  page of the caches given to pkd_run (not checked on device)
+ *   stream         the work list is uploaded with an asynchronous copy on it
+ * On success *out owns device memory and pinned host memory until
+ * pkd_plan_destroy. Not capturable in a HIP graph (it allocates). Errors:
+ * PKD_EINVAL (page table or parameter out of range, null pointer),
+ * PKD_EUNSUPPORTED (head_dim, G, page_size or dtype combination not built),
+ * PKD_ENOMEM / PKD_EHIP. */
+pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
+                           const int32_t* last_page_len, const int32_t* indices,
+                           void* stream, pkd_plan** out);
+
+/* Host-only planning: the same validation and chunking as pkd_plan_create for
+ * a GPU with `num_cus` compute units, without any HIP call. Writes *info and,
+ * if items != NULL, up to `capacity` work items in launch order. */
+pkd_status pkd_plan_query(const pkd_plan_params* params, const int32_t* indptr,
+                          const int32_t* last_page_len, int32_t num_cus,
+                          pkd_plan_info* info, pkd_work_item* items,
+                          int32_t capacity);
+
+pkd_status pkd_plan_get_info(const pkd_plan* plan, pkd_plan_info* info);
+
+/* Waits for the plan's upload to finish, then frees it. NULL is a no-op. */
+void pkd_plan_destroy(pkd_plan* plan);
+
+/* run() (flashinfer.decode › BatchDecodeWithPagedKVCacheWrapper › run()):
+ *   q        device, [B][num_qo_heads][head_dim] in q_dtype, contiguous
+ *   k_cache  device, K pages in kv_dtype and the plan's layout
+ *   v_cache  device, V pages; for the 5-D cache [pages][2][...] pass
+ *            v_cache = k_cache + P*num_kv_heads*head_dim elements
+ *   page_stride  elements from one page to the next in k_cache and v_cache:
+ *            2*P*num_kv_heads*head_dim for the 5-D cache,
+ *            P*num_kv_heads*head_dim for a (k_cache, v_cache) pair
+ *   q_scale, k_scale, v_scale  calibration scales (1.0 = none)
+ *   o        device, [B][num_qo_heads][head_dim] in o_dtype, written
+ *   lse      device, [B][num_qo_heads] fp32 natural-log LSE, or NULL
+ *   workspace, workspace_bytes  device scratch of at least
+ *            pkd_plan_info.workspace_bytes (may be NULL when that is 0); its
+ *            contents need no initialisation
+ * Launches the decode kernel and, if some request was split, the merge.
+ * Errors: PKD_EINVAL (null pointer, page_stride too small),
+ * PKD_EWORKSPACE, PKD_EHIP (launch failure). */
+pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
+                   const void* v_cache, int64_t page_stride, float q_scale,
+                   float k_scale, float v_scale, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* The two launches of pkd_run, callable separately (same arguments): the
+ * decode kernel writes o/lse of unsplit requests and the partial states of
+ * split ones; the merge then folds the partials, chunk by chunk in ascending
+ * order, into o/lse. pkd_run_merge is a no-op when no request was split. */
+pkd_status pkd_run_decode(const pkd_plan* plan, const void* q,
+                          const void* k_cache, const void* v_cache,
+                          int64_t page_stride, float q_scale, float k_scale,
+                          float v_scale, void* o, float* lse, void* workspace,
+                          size_t workspace_bytes, void* stream);
+pkd_status pkd_run_merge(const pkd_plan* plan, void* o, float* lse,
+                         const void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/* merge_states (named with fixed_split_size in plan()): combine `num_states`
+ * attention states per row by log-sum-exp, in ascending state order.
+ *   v      device fp32 [rows][num_states][head_dim], per-state normalised o
+ *   s      device fp32 [rows][num_states], per-state natural-log LSE;
+ *          -inf marks an empty state, which contributes nothing
+ *   v_out  device [rows][head_dim] in out_dtype (F16, BF16 or F32)
+ *   s_out  device fp32 [rows] natural-log LSE, or NULL
+ * A row whose states are all empty gets v_out = 0 and s_out = -inf.
+ * head_dim is 1 .. 1024. Errors: PKD_EINVAL, PKD_EUNSUPPORTED, PKD_EHIP. */
+pkd_status pkd_merge_states(const float* v, const float* s, int32_t rows,
+                            int32_t num_states, int32_t head_dim, void* v_out,
+                            int32_t out_dtype, float* s_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKD_H_ */

@@ -1,1 +1,398 @@
-"""Paged-KV batch decode attention for AMD MI355X (gfx950)."""
+"""Paged-KV batch decode attention for AMD MI355X (gfx950).
+
+A thin ctypes binding over the C-ABI library ``libpkd.so`` (include/pkd.h).
+This module only marshals arguments: torch provides device memory and the
+current stream, and every step of the computation runs in the library's HIP
+kernels. If the library is missing the calls raise; there is no fallback.
+
+Names follow flashinfer.decode.BatchDecodeWithPagedKVCacheWrapper on the
+"FlashInfer attention kernels" page (plan() / run() parameters).
+"""
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkd.so")
+
+PKD_OK, PKD_EINVAL, PKD_EUNSUPPORTED, PKD_EHIP, PKD_ENOMEM, PKD_EWORKSPACE = (
+    0, -1, -2, -3, -4, -5)
+PKD_F16, PKD_BF16, PKD_E4M3, PKD_F32 = 0, 1, 2, 3
+PKD_NHD, PKD_HND = 0, 1
+
+_STATUS = {PKD_EINVAL: "EINVAL", PKD_EUNSUPPORTED: "EUNSUPPORTED",
+           PKD_EHIP: "EHIP", PKD_ENOMEM: "ENOMEM", PKD_EWORKSPACE: "EWORKSPACE"}
+
+
+class PkdError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"pkd {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class pkd_plan_params(ctypes.Structure):
+    _fields_ = [("batch_size", ctypes.c_int32), ("num_qo_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("o_dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("logits_soft_cap", ctypes.c_float),
+                ("window_left", ctypes.c_int32),
+                ("fixed_split_size", ctypes.c_int32),
+                ("disable_split_kv", ctypes.c_int32)]
+
+
+class pkd_work_item(ctypes.Structure):
+    _fields_ = [("request", ctypes.c_int32), ("kv_head", ctypes.c_int32),
+                ("token_begin", ctypes.c_int32), ("token_end", ctypes.c_int32),
+                ("page_base", ctypes.c_int32), ("partial", ctypes.c_int32),
+                ("chunk", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class pkd_plan_info(ctypes.Structure):
+    _fields_ = [("num_items", ctypes.c_int32),
+                ("num_split_requests", ctypes.c_int32),
+                ("num_partials", ctypes.c_int32),
+                ("split_pages", ctypes.c_int32),
+                ("attended_tokens", ctypes.c_int64),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "pkd_abi_version": (ctypes.c_int32, []),
+    "pkd_last_error": (ctypes.c_char_p, []),
+    "pkd_plan_create": (ctypes.c_int, [ctypes.POINTER(pkd_plan_params), _P, _P,
+                                       _P, _P, ctypes.POINTER(_P)]),
+    "pkd_plan_query": (ctypes.c_int, [ctypes.POINTER(pkd_plan_params), _P, _P,
+                                      ctypes.c_int32,
+                                      ctypes.POINTER(pkd_plan_info), _P,
+                                      ctypes.c_int32]),
+    "pkd_plan_get_info": (ctypes.c_int, [_P, ctypes.POINTER(pkd_plan_info)]),
+    "pkd_plan_destroy": (None, [_P]),
+    "pkd_run": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_float,
+                               ctypes.c_float, ctypes.c_float, _P, _P, _P,
+                               ctypes.c_size_t, _P]),
+    "pkd_run_decode": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64,
+                                      ctypes.c_float, ctypes.c_float,
+                                      ctypes.c_float, _P, _P, _P,
+                                      ctypes.c_size_t, _P]),
+    "pkd_run_merge": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "pkd_merge_states": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, _P, ctypes.c_int32, _P,
+                                        _P]),
+}
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C-ABI library; raises if it was not built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m paged_kv_decode_09_amd.build` (no fallback exists)")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        if h.pkd_abi_version() != 1:
+            raise ImportError("libpkd.so ABI version mismatch")
+        _lib_handle = h
+    return _lib_handle
+
+
+def _check(status: int) -> None:
+    if status != PKD_OK:
+        raise PkdError(status, lib().pkd_last_error().decode())
+
+
+def _dtype_code(dt) -> int:
+    if isinstance(dt, str):
+        dt = {"float16": torch.float16, "half": torch.float16,
+              "bfloat16": torch.bfloat16, "float8_e4m3fn": torch.float8_e4m3fn,
+              "f16": torch.float16, "bf16": torch.bfloat16,
+              "e4m3": torch.float8_e4m3fn}[dt]
+    if dt == torch.float16:
+        return PKD_F16
+    if dt == torch.bfloat16:
+        return PKD_BF16
+    if dt in (torch.float8_e4m3fn, torch.uint8):
+        return PKD_E4M3
+    if dt == torch.float32:
+        return PKD_F32
+    raise PkdError(PKD_EUNSUPPORTED, f"dtype {dt} is not supported")
+
+
+_TORCH_OF = {PKD_F16: torch.float16, PKD_BF16: torch.bfloat16,
+             PKD_F32: torch.float32}
+
+
+def _host_i32(x) -> np.ndarray:
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _stream_ptr(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def make_params(batch_size, num_qo_heads, num_kv_heads, head_dim, page_size,
+                kv_layout="NHD", window_left=-1, logits_soft_cap=None,
+                q_data_type=torch.float16, kv_data_type=None,
+                o_data_type=None, sm_scale=None, fixed_split_size=None,
+                disable_split_kv=False) -> pkd_plan_params:
+    q_code = _dtype_code(q_data_type)
+    kv_code = q_code if kv_data_type is None else _dtype_code(kv_data_type)
+    o_code = q_code if o_data_type is None else _dtype_code(o_data_type)
+    if kv_layout not in ("NHD", "HND"):
+        raise PkdError(PKD_EINVAL, f"kv_layout {kv_layout!r} not NHD/HND")
+    return pkd_plan_params(
+        batch_size=int(batch_size), num_qo_heads=int(num_qo_heads),
+        num_kv_heads=int(num_kv_heads), head_dim=int(head_dim),
+        page_size=int(page_size),
+        layout=PKD_NHD if kv_layout == "NHD" else PKD_HND,
+        q_dtype=q_code, kv_dtype=kv_code, o_dtype=o_code,
+        sm_scale=(1.0 / math.sqrt(head_dim)) if sm_scale is None else sm_scale,
+        logits_soft_cap=0.0 if not logits_soft_cap else logits_soft_cap,
+        window_left=int(window_left),
+        fixed_split_size=0 if not fixed_split_size else int(fixed_split_size),
+        disable_split_kv=int(bool(disable_split_kv)))
+
+
+def plan_query(indptr, last_page_len, num_cus: int = 256, **kw):
+    """Host-only planning (no GPU): (pkd_plan_info, list of work items)."""
+    ip, lp = _host_i32(indptr), _host_i32(last_page_len)
+    params = make_params(len(lp), **kw)
+    info = pkd_plan_info()
+    _check(lib().pkd_plan_query(ctypes.byref(params), ip.ctypes.data,
+                                lp.ctypes.data, num_cus, ctypes.byref(info),
+                                None, 0))
+    items = (pkd_work_item * max(info.num_items, 1))()
+    _check(lib().pkd_plan_query(ctypes.byref(params), ip.ctypes.data,
+                                lp.ctypes.data, num_cus, ctypes.byref(info),
+                                ctypes.cast(items, _P), info.num_items))
+    return info, list(items)[:info.num_items]
+
+
+def _split_cache(paged_kv_cache, layout: int, page_size: int,
+                 num_kv_heads: int, head_dim: int):
+    """(k pointer, v pointer, page stride in elements, dtype) of a cache."""
+    page = (page_size, num_kv_heads, head_dim) if layout == PKD_NHD else (
+        num_kv_heads, page_size, head_dim)
+    inner = (num_kv_heads * head_dim, head_dim, 1) if layout == PKD_NHD else (
+        page_size * head_dim, head_dim, 1)
+    if isinstance(paged_kv_cache, (tuple, list)):
+        k, v = paged_kv_cache
+        for t in (k, v):
+            if t.dim() != 4 or tuple(t.shape[1:]) != page or \
+                    tuple(t.stride()[1:]) != inner:
+                raise PkdError(PKD_EINVAL, f"cache tensor {tuple(t.shape)} is "
+                               f"not [pages, {', '.join(map(str, page))}] "
+                               "with contiguous pages")
+        if k.stride(0) != v.stride(0) or k.dtype != v.dtype:
+            raise PkdError(PKD_EINVAL, "k_cache and v_cache must share the "
+                           "page stride and dtype")
+        return k.data_ptr(), v.data_ptr(), k.stride(0), k.dtype
+    c = paged_kv_cache
+    if c.dim() != 5 or c.shape[1] != 2 or tuple(c.shape[2:]) != page or \
+            tuple(c.stride()[2:]) != inner or \
+            c.stride(1) != page_size * num_kv_heads * head_dim:
+        raise PkdError(PKD_EINVAL, f"cache {tuple(c.shape)} is not "
+                       f"[pages, 2, {', '.join(map(str, page))}] with "
+                       "contiguous pages")
+    kp = c.data_ptr()
+    return kp, kp + c.stride(1) * c.element_size(), c.stride(0), c.dtype
+
+
+class PagedDecodePlan:
+    """One plan (pkd_plan_create): a batch's page table, reused across runs."""
+
+    def __init__(self, indptr, indices: torch.Tensor, last_page_len,
+                 num_qo_heads: int, num_kv_heads: int, head_dim: int,
+                 page_size: int, kv_layout: str = "NHD", window_left: int = -1,
+                 logits_soft_cap: Optional[float] = None,
+                 q_data_type=torch.float16, kv_data_type=None,
+                 o_data_type=None, sm_scale: Optional[float] = None,
+                 fixed_split_size: Optional[int] = None,
+                 disable_split_kv: bool = False, stream=None):
+        self._handle = None
+        ip, lp = _host_i32(indptr), _host_i32(last_page_len)
+        if indices.dtype != torch.int32 or not indices.is_cuda:
+            raise PkdError(PKD_EINVAL, "indices must be an int32 device tensor")
+        self.params = make_params(len(lp), num_qo_heads, num_kv_heads, head_dim,
+                                  page_size, kv_layout, window_left,
+                                  logits_soft_cap, q_data_type, kv_data_type,
+                                  o_data_type, sm_scale, fixed_split_size,
+                                  disable_split_kv)
+        self.indices = indices.contiguous()   # borrowed by the plan: keep alive
+        h = _P()
+        _check(lib().pkd_plan_create(ctypes.byref(self.params), ip.ctypes.data,
+                                     lp.ctypes.data, self.indices.data_ptr(),
+                                     _stream_ptr(stream), ctypes.byref(h)))
+        self._handle = h
+        self.info = pkd_plan_info()
+        _check(lib().pkd_plan_get_info(self._handle, ctypes.byref(self.info)))
+
+    def __del__(self):
+        if getattr(self, "_handle", None) is not None and _lib_handle is not None:
+            _lib_handle.pkd_plan_destroy(self._handle)
+            self._handle = None
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(self.info.workspace_bytes)
+
+    def _args(self, q, paged_kv_cache, q_scale, k_scale, v_scale, out, lse,
+              return_lse, workspace):
+        p = self.params
+        B, nq, hd = p.batch_size, p.num_qo_heads, p.head_dim
+        if tuple(q.shape) != (B, nq, hd) or not q.is_contiguous():
+            raise PkdError(PKD_EINVAL, f"q must be contiguous [{B}, {nq}, {hd}]")
+        if _dtype_code(q.dtype) != p.q_dtype:
+            raise PkdError(PKD_EINVAL, f"q dtype {q.dtype} differs from the plan")
+        kp, vp, stride, kv_dtype = _split_cache(paged_kv_cache, p.layout,
+                                                p.page_size, p.num_kv_heads, hd)
+        if _dtype_code(kv_dtype) != p.kv_dtype:
+            raise PkdError(PKD_EINVAL, f"cache dtype {kv_dtype} differs from "
+                           "the plan")
+        if out is None:
+            out = torch.empty((B, nq, hd), dtype=_TORCH_OF[p.o_dtype],
+                              device=q.device)
+        elif tuple(out.shape) != (B, nq, hd) or not out.is_contiguous() or \
+                _dtype_code(out.dtype) != p.o_dtype:
+            raise PkdError(PKD_EINVAL, "out has the wrong shape or dtype")
+        if return_lse and lse is None:
+            lse = torch.empty((B, nq), dtype=torch.float32, device=q.device)
+        ws_bytes = self.workspace_bytes
+        if workspace is None and ws_bytes > 0:
+            workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_len = workspace.numel() * workspace.element_size() if \
+            workspace is not None else 0
+        sc = [1.0 if s is None else float(s) for s in (q_scale, k_scale, v_scale)]
+        return (q, kp, vp, stride, sc, out, lse, ws_ptr, ws_len, workspace)
+
+    def run(self, q: torch.Tensor, paged_kv_cache, q_scale=None, k_scale=None,
+            v_scale=None, out=None, lse=None, return_lse: bool = False,
+            workspace: Optional[torch.Tensor] = None, stream=None):
+        """o [B, num_qo_heads, head_dim], or (o, lse) when return_lse."""
+        (q, kp, vp, stride, sc, out, lse, ws_ptr, ws_len,
+         _ws) = self._args(q, paged_kv_cache, q_scale, k_scale, v_scale, out,
+                           lse, return_lse or lse is not None, workspace)
+        _check(lib().pkd_run(self._handle, q.data_ptr(), kp, vp, stride,
+                             sc[0], sc[1], sc[2], out.data_ptr(),
+                             lse.data_ptr() if lse is not None else None,
+                             ws_ptr, ws_len, _stream_ptr(stream)))
+        return (out, lse) if return_lse else out
+
+    def run_decode(self, q, paged_kv_cache, q_scale=None, k_scale=None,
+                   v_scale=None, out=None, lse=None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+        """The decode launch alone (pkd_run_decode)."""
+        (q, kp, vp, stride, sc, out, lse, ws_ptr, ws_len,
+         _ws) = self._args(q, paged_kv_cache, q_scale, k_scale, v_scale, out,
+                           lse, lse is not None, workspace)
+        _check(lib().pkd_run_decode(self._handle, q.data_ptr(), kp, vp, stride,
+                                    sc[0], sc[1], sc[2], out.data_ptr(),
+                                    lse.data_ptr() if lse is not None else None,
+                                    ws_ptr, ws_len, _stream_ptr(stream)))
+        return out, lse
+
+    def run_merge(self, out, lse, workspace, stream=None):
+        """The merge launch alone (pkd_run_merge)."""
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_len = workspace.numel() * workspace.element_size() if \
+            workspace is not None else 0
+        _check(lib().pkd_run_merge(self._handle, out.data_ptr(),
+                                   lse.data_ptr() if lse is not None else None,
+                                   ws_ptr, ws_len, _stream_ptr(stream)))
+        return out, lse
+
+
+class BatchDecodeWithPagedKVCacheWrapper:
+    """plan()/run() in the shape of the wrapper on the FlashInfer page.
+
+    ``float_workspace_buffer`` is a uint8 device tensor used for split-KV
+    partial states; it is grown (reallocated) if a plan needs more.
+    """
+
+    def __init__(self, float_workspace_buffer: torch.Tensor,
+                 kv_layout: str = "NHD"):
+        self._ws = float_workspace_buffer
+        self._layout = kv_layout
+        self._plan: Optional[PagedDecodePlan] = None
+
+    def reset_workspace_buffer(self, float_workspace_buffer: torch.Tensor,
+                               int_workspace_buffer=None) -> None:
+        self._ws = float_workspace_buffer
+
+    def plan(self, indptr, indices, last_page_len, num_qo_heads, num_kv_heads,
+             head_dim, page_size, pos_encoding_mode="NONE", window_left=-1,
+             logits_soft_cap=None, q_data_type=torch.float16,
+             kv_data_type=None, o_data_type=None, data_type=None,
+             sm_scale=None, rope_scale=None, rope_theta=None,
+             non_blocking=True, fixed_split_size=None,
+             disable_split_kv=False) -> None:
+        if pos_encoding_mode != "NONE":
+            raise PkdError(PKD_EUNSUPPORTED,
+                           f"pos_encoding_mode {pos_encoding_mode!r}")
+        if data_type is not None:
+            q_data_type = data_type
+            kv_data_type = kv_data_type or data_type
+        self._plan = PagedDecodePlan(
+            indptr, indices.to(torch.int32), last_page_len, num_qo_heads,
+            num_kv_heads, head_dim, page_size, self._layout, window_left,
+            logits_soft_cap, q_data_type, kv_data_type, o_data_type, sm_scale,
+            fixed_split_size, disable_split_kv)
+        need = self._plan.workspace_bytes
+        if self._ws.numel() * self._ws.element_size() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8,
+                                   device=self._ws.device)
+
+    def run(self, q, paged_kv_cache, q_scale=None, k_scale=None, v_scale=None,
+            out=None, lse=None, return_lse=False):
+        if self._plan is None:
+            raise PkdError(PKD_EINVAL, "run() before plan()")
+        ws = self._ws if self._plan.workspace_bytes > 0 else None
+        return self._plan.run(q, paged_kv_cache, q_scale, k_scale, v_scale,
+                              out, lse, return_lse, ws)
+
+
+def merge_states(v: torch.Tensor, s: torch.Tensor, out_dtype=None,
+                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Merge attention states (pkd_merge_states).
+
+    v: fp32 [rows, num_states, head_dim]; s: fp32 [rows, num_states]
+    natural-log LSE. Returns (v_merged [rows, head_dim], s_merged [rows]).
+    """
+    if v.dtype != torch.float32 or s.dtype != torch.float32 or \
+            v.dim() != 3 or s.shape != v.shape[:2]:
+        raise PkdError(PKD_EINVAL, "v must be fp32 [rows, n, hd] and s fp32 "
+                       "[rows, n]")
+    v, s = v.contiguous(), s.contiguous()
+    rows, n, hd = v.shape
+    od = torch.float32 if out_dtype is None else out_dtype
+    v_out = torch.empty((rows, hd), dtype=od, device=v.device)
+    s_out = torch.empty((rows,), dtype=torch.float32, device=v.device)
+    _check(lib().pkd_merge_states(v.data_ptr(), s.data_ptr(), rows, n, hd,
+                                  v_out.data_ptr(), _dtype_code(od),
+                                  s_out.data_ptr(), _stream_ptr(stream)))
+    return v_out, s_out
+
+
+__all__ = ["lib", "PkdError", "PagedDecodePlan",
+           "BatchDecodeWithPagedKVCacheWrapper", "merge_states", "plan_query",
+           "make_params", "pkd_plan_params", "pkd_plan_info", "pkd_work_item"]

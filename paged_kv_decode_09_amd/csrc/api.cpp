@@ -1,0 +1,294 @@
+// C-ABI of the paged-KV batch decode library (declared in include/pkd.h).
+//
+// plan/run split of flashinfer.decode.BatchDecodeWithPagedKVCacheWrapper
+// ("FlashInfer attention kernels" page): plan() does the host work once and
+// uploads the work list; run() only enqueues kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "pkd_internal.h"
+
+struct pkd_plan {
+  pkd::HostPlan host;
+  const int32_t* indices = nullptr;   // borrowed device pointer
+  void* dev = nullptr;                // items followed by merge rows
+  void* staging = nullptr;            // pinned host copy used by the upload
+  hipEvent_t uploaded = nullptr;
+  int device = 0;
+  const pkd_work_item* d_items() const {
+    return reinterpret_cast<const pkd_work_item*>(dev);
+  }
+  const pkd::MergeRow* d_merges() const {
+    return reinterpret_cast<const pkd::MergeRow*>(
+        reinterpret_cast<const char*>(dev) +
+        host.items.size() * sizeof(pkd_work_item));
+  }
+};
+
+namespace {
+
+pkd_status hip_fail(hipError_t e, const char* what) {
+  return pkd::fail(PKD_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+void free_plan(pkd_plan* p) {
+  if (p == nullptr) return;
+  if (p->uploaded != nullptr) {
+    (void)hipEventSynchronize(p->uploaded);
+    (void)hipEventDestroy(p->uploaded);
+  }
+  if (p->dev != nullptr) (void)hipFree(p->dev);
+  if (p->staging != nullptr) (void)hipHostFree(p->staging);
+  delete p;
+}
+
+size_t plan_bytes(const pkd::HostPlan& h) {
+  return h.items.size() * sizeof(pkd_work_item) +
+         h.merges.size() * sizeof(pkd::MergeRow);
+}
+
+pkd_status check_run(const pkd_plan* plan, const void* q, const void* k,
+                     const void* v, int64_t page_stride, void* o,
+                     void* workspace, size_t workspace_bytes) {
+  if (plan == nullptr) return pkd::fail(PKD_EINVAL, "plan is NULL (run before plan)");
+  const pkd_plan_params& p = plan->host.params;
+  if (p.batch_size == 0) return PKD_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+    return pkd::fail(PKD_EINVAL, "q, k_cache, v_cache and o must not be NULL");
+  const int64_t page_elems = (int64_t)p.page_size * p.num_kv_heads * p.head_dim;
+  if (page_stride < page_elems)
+    return pkd::fail(PKD_EINVAL, "page_stride " + std::to_string(page_stride) +
+                                     " < page_size*num_kv_heads*head_dim = " +
+                                     std::to_string(page_elems));
+  const int kv_bytes = p.kv_dtype == PKD_E4M3 ? 1 : 2;
+  if ((page_stride * kv_bytes) % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(k) % 16) != 0 ||
+      (reinterpret_cast<uintptr_t>(v) % 16) != 0 ||
+      (reinterpret_cast<uintptr_t>(q) % 16) != 0)
+    return pkd::fail(PKD_EINVAL,
+                     "q, k_cache and v_cache must be 16-byte aligned and the page "
+                     "stride a multiple of 16 bytes");
+  const size_t need = plan->host.info.workspace_bytes;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need))
+    return pkd::fail(PKD_EWORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
+                                         " bytes < required " + std::to_string(need));
+  if (need > 0 && reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return pkd::fail(PKD_EINVAL, "workspace must be 256-byte aligned");
+  return PKD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkd_abi_version(void) { return PKD_ABI_VERSION; }
+
+pkd_status pkd_plan_query(const pkd_plan_params* params, const int32_t* indptr,
+                          const int32_t* last_page_len, int32_t num_cus,
+                          pkd_plan_info* info, pkd_work_item* items,
+                          int32_t capacity) {
+  if (params == nullptr || info == nullptr)
+    return pkd::fail(PKD_EINVAL, "params and info must not be NULL");
+  pkd::HostPlan h;
+  pkd_status st = pkd::build_host_plan(*params, indptr, last_page_len, num_cus, &h);
+  if (st != PKD_OK) return st;
+  *info = h.info;
+  if (items != nullptr) {
+    const size_t n = std::min<size_t>(h.items.size(), capacity < 0 ? 0 : (size_t)capacity);
+    std::memcpy(items, h.items.data(), n * sizeof(pkd_work_item));
+  }
+  return PKD_OK;
+}
+
+pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
+                           const int32_t* last_page_len, const int32_t* indices,
+                           void* stream, pkd_plan** out) {
+  if (out == nullptr) return pkd::fail(PKD_EINVAL, "out must not be NULL");
+  *out = nullptr;
+  if (params == nullptr) return pkd::fail(PKD_EINVAL, "params must not be NULL");
+  pkd_status st = pkd::check_params(*params);
+  if (st != PKD_OK) return st;
+  if (params->batch_size > 0 && indices == nullptr)
+    return pkd::fail(PKD_EINVAL, "indices must not be NULL");
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+
+  pkd_plan* p = new (std::nothrow) pkd_plan();
+  if (p == nullptr) return pkd::fail(PKD_ENOMEM, "plan allocation failed");
+  st = pkd::build_host_plan(*params, indptr, last_page_len, cus, &p->host);
+  if (st != PKD_OK) {
+    delete p;
+    return st;
+  }
+  p->indices = indices;
+  p->device = dev;
+  const size_t bytes = plan_bytes(p->host);
+  if (bytes > 0) {
+    e = hipMalloc(&p->dev, bytes);
+    if (e != hipSuccess) {
+      free_plan(p);
+      return pkd::fail(PKD_ENOMEM, std::string("hipMalloc of the work list: ") +
+                                       hipGetErrorString(e));
+    }
+    e = hipHostMalloc(&p->staging, bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      free_plan(p);
+      return pkd::fail(PKD_ENOMEM, std::string("hipHostMalloc of the staging copy: ") +
+                                       hipGetErrorString(e));
+    }
+    char* s = reinterpret_cast<char*>(p->staging);
+    std::memcpy(s, p->host.items.data(), p->host.items.size() * sizeof(pkd_work_item));
+    std::memcpy(s + p->host.items.size() * sizeof(pkd_work_item), p->host.merges.data(),
+                p->host.merges.size() * sizeof(pkd::MergeRow));
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    e = hipMemcpyAsync(p->dev, p->staging, bytes, hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(p->uploaded, hs);
+    if (e != hipSuccess) {
+      (void)hipStreamSynchronize(hs);
+      free_plan(p);
+      return hip_fail(e, "uploading the work list");
+    }
+  }
+  *out = p;
+  pkd::clear_error();
+  return PKD_OK;
+}
+
+pkd_status pkd_plan_get_info(const pkd_plan* plan, pkd_plan_info* info) {
+  if (plan == nullptr || info == nullptr)
+    return pkd::fail(PKD_EINVAL, "plan and info must not be NULL");
+  *info = plan->host.info;
+  return PKD_OK;
+}
+
+void pkd_plan_destroy(pkd_plan* plan) { free_plan(plan); }
+
+pkd_status pkd_run_decode(const pkd_plan* plan, const void* q, const void* k_cache,
+                          const void* v_cache, int64_t page_stride, float q_scale,
+                          float k_scale, float v_scale, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  pkd_status st = check_run(plan, q, k_cache, v_cache, page_stride, o, workspace,
+                            workspace_bytes);
+  if (st != PKD_OK) return st;
+  const pkd_plan_params& p = plan->host.params;
+  if (plan->host.items.empty()) return PKD_OK;
+  if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return pkd::fail(PKD_EINVAL, "q_scale, k_scale and v_scale must be finite");
+  pkd::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.indices = plan->indices;
+  a.items = plan->d_items();
+  a.o = o;
+  a.lse = lse;
+  const int32_t parts = plan->host.info.num_partials;
+  a.ws_o = reinterpret_cast<float*>(workspace);
+  a.ws_lse = parts > 0 ? reinterpret_cast<float*>(
+                             reinterpret_cast<char*>(workspace) +
+                             pkd::workspace_lse_offset(parts, p.num_qo_heads, p.head_dim))
+                       : nullptr;
+  a.page_stride = page_stride;
+  if (p.layout == PKD_NHD) {
+    a.slot_stride = p.num_kv_heads * p.head_dim;
+    a.head_stride = p.head_dim;
+  } else {
+    a.slot_stride = p.head_dim;
+    a.head_stride = p.page_size * p.head_dim;
+  }
+  a.num_qo_heads = p.num_qo_heads;
+  a.group = p.num_qo_heads / p.num_kv_heads;
+  int lg = 0;
+  while ((1 << lg) < p.page_size) ++lg;
+  a.log2_page = lg;
+  a.o_bf16 = p.o_dtype == PKD_BF16;
+  const float scale = p.sm_scale * q_scale * k_scale;
+  const bool cap = p.logits_soft_cap > 0.0f;
+  a.logit_scale = cap ? scale : scale * 1.4426950408889634f;
+  a.cap = cap ? p.logits_soft_cap : 0.0f;
+  a.inv_cap = cap ? 1.0f / p.logits_soft_cap : 0.0f;
+  a.v_scale = v_scale;
+  int e = pkd::launch_decode(p, a, plan->host.info.num_items, stream);
+  if (e != hipSuccess) return hip_fail((hipError_t)e, "decode launch");
+  return PKD_OK;
+}
+
+pkd_status pkd_run_merge(const pkd_plan* plan, void* o, float* lse,
+                         const void* workspace, size_t workspace_bytes, void* stream) {
+  if (plan == nullptr) return pkd::fail(PKD_EINVAL, "plan is NULL (run before plan)");
+  const pkd_plan_params& p = plan->host.params;
+  const int32_t parts = plan->host.info.num_partials;
+  if (parts == 0) return PKD_OK;
+  if (o == nullptr) return pkd::fail(PKD_EINVAL, "o must not be NULL");
+  if (workspace == nullptr || workspace_bytes < plan->host.info.workspace_bytes)
+    return pkd::fail(PKD_EWORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
+                                         " bytes < required " +
+                                         std::to_string(plan->host.info.workspace_bytes));
+  pkd::MergeArgs m{};
+  m.v = reinterpret_cast<const float*>(workspace);
+  m.s = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) +
+                                       pkd::workspace_lse_offset(parts, p.num_qo_heads,
+                                                                 p.head_dim));
+  m.rows = plan->d_merges();
+  m.v_out = o;
+  m.s_out = lse;
+  m.num_rows = plan->host.info.num_split_requests * p.num_qo_heads;
+  m.num_states = 0;
+  m.head_dim = p.head_dim;
+  m.num_qo_heads = p.num_qo_heads;
+  m.out_dtype = p.o_dtype;
+  m.s_base2 = 1;
+  int e = pkd::launch_merge(m, stream);
+  if (e != hipSuccess) return hip_fail((hipError_t)e, "merge launch");
+  return PKD_OK;
+}
+
+pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
+                   const void* v_cache, int64_t page_stride, float q_scale,
+                   float k_scale, float v_scale, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  pkd_status st = pkd_run_decode(plan, q, k_cache, v_cache, page_stride, q_scale,
+                                 k_scale, v_scale, o, lse, workspace, workspace_bytes,
+                                 stream);
+  if (st != PKD_OK) return st;
+  return pkd_run_merge(plan, o, lse, workspace, workspace_bytes, stream);
+}
+
+pkd_status pkd_merge_states(const float* v, const float* s, int32_t rows,
+                            int32_t num_states, int32_t head_dim, void* v_out,
+                            int32_t out_dtype, float* s_out, void* stream) {
+  if (rows < 0 || num_states < 0)
+    return pkd::fail(PKD_EINVAL, "rows and num_states must be >= 0");
+  if (head_dim < 1 || head_dim > 1024)
+    return pkd::fail(PKD_EUNSUPPORTED, "head_dim " + std::to_string(head_dim) +
+                                           " outside [1, 1024]");
+  if (out_dtype != PKD_F16 && out_dtype != PKD_BF16 && out_dtype != PKD_F32)
+    return pkd::fail(PKD_EUNSUPPORTED, "out_dtype must be F16, BF16 or F32");
+  if (rows == 0) return PKD_OK;
+  if (v_out == nullptr || (num_states > 0 && (v == nullptr || s == nullptr)))
+    return pkd::fail(PKD_EINVAL, "v, s and v_out must not be NULL");
+  pkd::MergeArgs m{};
+  m.v = v;
+  m.s = s;
+  m.rows = nullptr;
+  m.v_out = v_out;
+  m.s_out = s_out;
+  m.num_rows = rows;
+  m.num_states = num_states;
+  m.head_dim = head_dim;
+  m.num_qo_heads = 1;
+  m.out_dtype = out_dtype;
+  m.s_base2 = 0;
+  int e = pkd::launch_merge(m, stream);
+  if (e != hipSuccess) return hip_fail((hipError_t)e, "merge launch");
+  return PKD_OK;
+}
+
+}  // extern "C"

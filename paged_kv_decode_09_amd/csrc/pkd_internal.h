@@ -1,0 +1,99 @@
+// Internal declarations shared by the planner, the C-ABI layer and the HIP
+// kernels of the paged-KV decode library. Not installed; callers use pkd.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "pkd.h"
+
+namespace pkd {
+
+// Workgroup geometry of the decode kernel: kWaves wavefronts of 64 lanes work
+// on one work item; each wavefront takes kStepTokens tokens per step.
+constexpr int kWaves = 4;
+constexpr int kStepTokens = 32;
+constexpr int kMaxGroup = 16;       // q heads per kv head (one MFMA tile)
+constexpr int kMergeRowsPerBlock = 4;
+
+// One request whose chunks must be merged: its workspace slots are
+// partial_base .. partial_base + num_chunks - 1, in chunk order.
+struct MergeRow {
+  int32_t request;
+  int32_t partial_base;
+  int32_t num_chunks;
+  int32_t reserved;
+};
+
+struct HostPlan {
+  pkd_plan_params params{};
+  pkd_plan_info info{};
+  std::vector<pkd_work_item> items;
+  std::vector<MergeRow> merges;
+};
+
+// Records `msg` as this thread's last error and returns `st`.
+pkd_status fail(pkd_status st, const std::string& msg);
+void clear_error();
+
+// Validation of the parameters alone (no page table).
+pkd_status check_params(const pkd_plan_params& p);
+
+// The planner: validates the page table, picks the chunk size and builds the
+// work list and merge list. Pure host code.
+pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
+                           const int32_t* last_page_len, int32_t num_cus,
+                           HostPlan* out);
+
+// Byte offset of the LSE part of the workspace.
+size_t workspace_lse_offset(int32_t num_partials, int32_t num_qo_heads,
+                            int32_t head_dim);
+
+// ----------------------------------------------------------------- kernels
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* indices;
+  const pkd_work_item* items;
+  void* o;
+  float* lse;
+  float* ws_o;          // [num_partials][num_qo_heads][head_dim]
+  float* ws_lse;        // [num_partials][num_qo_heads], base-2
+  int64_t page_stride;  // elements between pages
+  int32_t slot_stride;  // elements between tokens of a page
+  int32_t head_stride;  // elements between kv heads of a page
+  int32_t num_qo_heads;
+  int32_t group;        // G
+  int32_t log2_page;
+  int32_t o_bf16;       // output dtype: 0 = f16, 1 = bf16
+  float logit_scale;    // sm_scale*q_scale*k_scale (times log2 e if no cap)
+  float cap;            // soft cap (> 0 only in the capped kernels)
+  float inv_cap;
+  float v_scale;
+};
+
+struct MergeArgs {
+  const float* v;       // per-state outputs
+  const float* s;       // per-state LSE
+  const MergeRow* rows; // plan merge list (plan mode) or NULL (flat mode)
+  void* v_out;
+  float* s_out;
+  int32_t num_rows;     // rows to produce
+  int32_t num_states;   // flat mode: states per row
+  int32_t head_dim;
+  int32_t num_qo_heads; // plan mode: heads per request
+  int32_t out_dtype;    // pkd_dtype of v_out
+  int32_t s_base2;      // 1: s is log2-based (plan workspace); 0: natural
+};
+
+// Launch wrappers (decode.hip). Return a hipError_t value as int.
+int launch_decode(const pkd_plan_params& p, const DecodeArgs& a,
+                  int32_t num_items, void* stream);
+int launch_merge(const MergeArgs& a, void* stream);
+
+}  // namespace pkd
