@@ -86,7 +86,9 @@ typedef struct {
 } pkd_plan_params;
 
 /* One unit of decode work: the tokens [token_begin, token_end) of one chunk of
- * one request, for one kv head and its G q heads. */
+ * one request, for one kv head and its G q heads. Under a fixed split, chunks
+ * longer than 1024 tokens are processed as units of 1024 tokens cut at fixed
+ * offsets from the chunk start, so each unit depends on its request alone. */
 typedef struct {
   int32_t request;
   int32_t kv_head;
@@ -94,15 +96,17 @@ typedef struct {
   int32_t token_end;        /* one past the last attended token             */
   int32_t page_base;        /* indptr[request]                              */
   int32_t partial;          /* -1: writes o/lse; else its workspace slot    */
-  int32_t chunk;            /* chunk index within the request (ascending)   */
+  int32_t chunk;            /* unit index within the request (ascending)    */
   int32_t reserved;
 } pkd_work_item;
 
 typedef struct {
-  int32_t num_items;        /* work items = decode workgroups               */
-  int32_t num_split_requests; /* requests cut into more than one chunk      */
-  int32_t num_partials;     /* workspace slots (chunks of split requests)   */
+  int32_t num_items;        /* work items (units of decode work)            */
+  int32_t num_workgroups;   /* decode workgroups; they take items in order  */
+  int32_t num_split_requests; /* requests cut into more than one unit       */
+  int32_t num_partials;     /* workspace slots (units of split requests)    */
   int32_t split_pages;      /* chunk size in pages; 0 = no split            */
+  int32_t reserved;
   int64_t attended_tokens;  /* sum over requests of attended tokens         */
   size_t workspace_bytes;   /* bytes the workspace of pkd_run must hold     */
 } pkd_plan_info;
@@ -133,8 +137,10 @@ pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
                            void* stream, pkd_plan** out);
 
 /* Host-only planning: the same validation and chunking as pkd_plan_create for
- * a GPU with `num_cus` compute units, without any HIP call. Writes *info and,
- * if items != NULL, up to `capacity` work items in launch order. */
+ * a gfx950 GPU with `num_cus` compute units (the number of decode workgroups
+ * per compute unit is taken from the library's build), without any HIP call.
+ * Writes *info and, if items != NULL, up to `capacity` work items in the
+ * order the decode workgroups take them (longest first). */
 pkd_status pkd_plan_query(const pkd_plan_params* params, const int32_t* indptr,
                           const int32_t* last_page_len, int32_t num_cus,
                           pkd_plan_info* info, pkd_work_item* items,
@@ -160,6 +166,9 @@ void pkd_plan_destroy(pkd_plan* plan);
  *            pkd_plan_info.workspace_bytes (may be NULL when that is 0); its
  *            contents need no initialisation
  * Launches the decode kernel and, if some request was split, the merge.
+ * Runs of one plan must not overlap in time (for example on two streams):
+ * the decode workgroups share a work counter owned by the plan. Runs of
+ * different plans may overlap.
  * Errors: PKD_EINVAL (null pointer, page_stride too small),
  * PKD_EWORKSPACE, PKD_EHIP (launch failure). */
 pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,

@@ -55,9 +55,11 @@ class pkd_work_item(ctypes.Structure):
 
 class pkd_plan_info(ctypes.Structure):
     _fields_ = [("num_items", ctypes.c_int32),
+                ("num_workgroups", ctypes.c_int32),
                 ("num_split_requests", ctypes.c_int32),
                 ("num_partials", ctypes.c_int32),
                 ("split_pages", ctypes.c_int32),
+                ("reserved", ctypes.c_int32),
                 ("attended_tokens", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_size_t)]
 

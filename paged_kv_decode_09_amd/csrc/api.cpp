@@ -18,12 +18,17 @@ struct pkd_plan {
   void* staging = nullptr;            // pinned host copy used by the upload
   hipEvent_t uploaded = nullptr;
   int device = 0;
+  // device copy: the decode work counters (zeroed by the upload), the items,
+  // then the merge rows
+  static constexpr size_t kCounterBytes = 64;
+  int32_t* d_counters() const { return reinterpret_cast<int32_t*>(dev); }
   const pkd_work_item* d_items() const {
-    return reinterpret_cast<const pkd_work_item*>(dev);
+    return reinterpret_cast<const pkd_work_item*>(reinterpret_cast<const char*>(dev) +
+                                                  kCounterBytes);
   }
   const pkd::MergeRow* d_merges() const {
     return reinterpret_cast<const pkd::MergeRow*>(
-        reinterpret_cast<const char*>(dev) +
+        reinterpret_cast<const char*>(d_items()) +
         host.items.size() * sizeof(pkd_work_item));
   }
 };
@@ -46,7 +51,8 @@ void free_plan(pkd_plan* p) {
 }
 
 size_t plan_bytes(const pkd::HostPlan& h) {
-  return h.items.size() * sizeof(pkd_work_item) +
+  if (h.items.empty()) return 0;
+  return pkd_plan::kCounterBytes + h.items.size() * sizeof(pkd_work_item) +
          h.merges.size() * sizeof(pkd::MergeRow);
 }
 
@@ -93,7 +99,11 @@ pkd_status pkd_plan_query(const pkd_plan_params* params, const int32_t* indptr,
   if (params == nullptr || info == nullptr)
     return pkd::fail(PKD_EINVAL, "params and info must not be NULL");
   pkd::HostPlan h;
-  pkd_status st = pkd::build_host_plan(*params, indptr, last_page_len, num_cus, &h);
+  pkd_status st = pkd::check_params(*params);
+  if (st != PKD_OK) return st;
+  if (num_cus < 1) return pkd::fail(PKD_EINVAL, "num_cus " + std::to_string(num_cus) + " < 1");
+  st = pkd::build_host_plan(*params, indptr, last_page_len,
+                            num_cus * pkd::decode_wgs_per_cu_table(*params), &h);
   if (st != PKD_OK) return st;
   *info = h.info;
   if (items != nullptr) {
@@ -119,9 +129,11 @@ pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
 
+  const int32_t per_cu = pkd::decode_wgs_per_cu(*params);
+  if (per_cu < 1) return pkd::fail(PKD_EHIP, "occupancy query of the decode kernel failed");
   pkd_plan* p = new (std::nothrow) pkd_plan();
   if (p == nullptr) return pkd::fail(PKD_ENOMEM, "plan allocation failed");
-  st = pkd::build_host_plan(*params, indptr, last_page_len, cus, &p->host);
+  st = pkd::build_host_plan(*params, indptr, last_page_len, cus * per_cu, &p->host);
   if (st != PKD_OK) {
     delete p;
     return st;
@@ -143,9 +155,11 @@ pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
                                        hipGetErrorString(e));
     }
     char* s = reinterpret_cast<char*>(p->staging);
+    std::memset(s, 0, pkd_plan::kCounterBytes);
+    s += pkd_plan::kCounterBytes;
     std::memcpy(s, p->host.items.data(), p->host.items.size() * sizeof(pkd_work_item));
-    std::memcpy(s + p->host.items.size() * sizeof(pkd_work_item), p->host.merges.data(),
-                p->host.merges.size() * sizeof(pkd::MergeRow));
+    s += p->host.items.size() * sizeof(pkd_work_item);
+    std::memcpy(s, p->host.merges.data(), p->host.merges.size() * sizeof(pkd::MergeRow));
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     e = hipMemcpyAsync(p->dev, p->staging, bytes, hipMemcpyHostToDevice, hs);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming);
@@ -182,6 +196,8 @@ pkd_status pkd_run_decode(const pkd_plan* plan, const void* q, const void* k_cac
   if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return pkd::fail(PKD_EINVAL, "q_scale, k_scale and v_scale must be finite");
   pkd::DecodeArgs a{};
+  a.counters = plan->d_counters();
+  a.num_items = plan->host.info.num_items;
   a.q = q;
   a.k = k_cache;
   a.v = v_cache;
@@ -215,7 +231,7 @@ pkd_status pkd_run_decode(const pkd_plan* plan, const void* q, const void* k_cac
   a.cap = cap ? p.logits_soft_cap : 0.0f;
   a.inv_cap = cap ? 1.0f / p.logits_soft_cap : 0.0f;
   a.v_scale = v_scale;
-  int e = pkd::launch_decode(p, a, plan->host.info.num_items, stream);
+  int e = pkd::launch_decode(p, a, plan->host.info.num_workgroups, stream);
   if (e != hipSuccess) return hip_fail((hipError_t)e, "decode launch");
   return PKD_OK;
 }

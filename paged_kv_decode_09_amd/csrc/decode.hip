@@ -136,6 +136,12 @@ struct Geo {
   static constexpr int kPieces = kRowBytes / 64;
   static constexpr int kQkMfma = HD / 32;   // MFMAs per 16-token tile
   static constexpr int kPvMfma = HD / 16;   // MFMAs per 32-token step
+  // Wavefronts per SIMD the register budget is sized for: two steps of K/V
+  // rows live in registers (the next step's loads are issued before the
+  // current step is computed), which leaves room for two wavefronts per SIMD
+  // up to head_dim 128 and one at head_dim 256.
+  static constexpr int kWavesPerSimd = HD == 256 ? 1 : 2;
+  static constexpr int kStages = 2;
   // LDS row pitch of the V copy; the pad staggers rows across banks.
   static constexpr int kVPitch = kRowBytes + (KV8 ? 16 : 32);
   static constexpr int kVBytes = kStepTokens * kVPitch;
@@ -143,31 +149,72 @@ struct Geo {
   static constexpr int kWaveLds = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
 };
 
-// Byte offset, inside a K/V row, of the 8 operand elements that lane group g
-// feeds to QK MFMA j. The hd order inside the dot product is free as long as
-// q uses the same one.
+// Page ids of the item are staged in LDS, a window at a time, so that the
+// per-step page lookups do not queue behind the K/V loads in flight.
+constexpr int kPageWin = 1024;
+
+// hd index of the first of the 8 operand elements that lane group g feeds to
+// QK MFMA j. The hd order inside the dot product is free as long as q uses
+// the same one; this one makes each load instruction of a wave cover 64
+// contiguous bytes of a row.
 template <bool KV8>
 __device__ __forceinline__ int qk_hd(int j, int g) {
   return KV8 ? 64 * (j >> 1) + 16 * g + 8 * (j & 1) : 32 * j + 8 * g;
 }
 
+// The item list is read-only for the whole launch: read it through the
+// constant address space so that it arrives in scalar registers.
+__device__ __forceinline__ pkd_work_item load_item(const pkd_work_item* items, int k) {
+  const __attribute__((address_space(4))) int32_t* w =
+      (const __attribute__((address_space(4))) int32_t*)(items + k);
+  pkd_work_item it;
+  it.request = w[0];
+  it.kv_head = w[1];
+  it.token_begin = w[2];
+  it.token_end = w[3];
+  it.page_base = w[4];
+  it.partial = w[5];
+  it.chunk = w[6];
+  it.reserved = w[7];
+  return it;
+}
+
+template <int NP>
+struct StepRegs {
+  u32x4 k[2][NP];
+  u32x4 v[2][NP];
+};
+
 template <int HD, bool QBF16, bool KV8, bool CAP>
-__global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWaves * 64, HD == 256 ? 1 : 2) void decode_kernel(DecodeArgs a) {
   using G_ = Geo<HD, KV8>;
   using O = Op<QBF16>;
   using v8 = typename O::v8;
   __shared__ __attribute__((aligned(16))) char smem[kWaves * G_::kWaveLds];
+  __shared__ int s_pages[kPageWin];
   __shared__ float s_m[kWaves][kMaxGroup];
   __shared__ float s_d[kWaves][kMaxGroup];
 
-  const pkd_work_item it = a.items[blockIdx.x];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform (an SGPR), so that the step loop branches on scalars
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;        // MFMA row (tile token) / column (q head)
   const int g = lane >> 4;        // lane group
   const int group = a.group;
+  // Work items are taken in order from the plan's counter, one at a time per
+  // workgroup; the next one is requested when the current one starts.
+  __shared__ int s_item;
+  if (threadIdx.x == 0) s_item = atomicAdd(&a.counters[0], 1);
+  __syncthreads();
+  int item = __builtin_amdgcn_readfirstlane(s_item);   // uniform: scalar loads, scalar branches
+  while (item < a.num_items) {
+  // the item list is read-only for the whole launch: scalar loads
+  const pkd_work_item it = load_item(a.items, item);
+  int next = 0;
+  if (threadIdx.x == 0) next = atomicAdd(&a.counters[0], 1);
   const int tb = it.token_begin, te = it.token_end;
   const int qh0 = it.kv_head * group;
+  const int lp = a.log2_page;
 
   // ---- q operand: head n of this kv head (zero past G)
   v8 bq[G_::kQkMfma];
@@ -188,7 +235,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
   // rows 4g'+i then map to tokens 8g'+4*tile+i.
   const int tau0 = 8 * (n >> 2) + (n & 3);
   const int tau1 = tau0 + 4;
-  const int page_mask = (1 << a.log2_page) - 1;
+  const int page_mask = (1 << lp) - 1;
   const int32_t* pidx = a.indices + it.page_base;
   const int64_t head_off = (int64_t)it.kv_head * a.head_stride;
   const char* kbase = reinterpret_cast<const char*>(a.k);
@@ -201,63 +248,62 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int b = 0; b < G_::kPvMfma; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  auto clampt = [&](int t) { return min(max(t, tb), te - 1); };
-  int step = wave;
-  int pg0 = 0, pg1 = 0;
-  if (step < nsteps) {
-    const int t0 = base + step * kStepTokens;
-    pg0 = pidx[clampt(t0 + tau0) >> a.log2_page];
-    pg1 = pidx[clampt(t0 + tau1) >> a.log2_page];
-  }
-  for (; step < nsteps; step += kWaves) {
-    const int t0 = base + step * kStepTokens;
-    const int c0 = clampt(t0 + tau0), c1 = clampt(t0 + tau1);
+  // Tokens of the current LDS page window are [wlo, whi]; loads of tokens
+  // outside it (masked ones, and the surplus prefetch past the last step) are
+  // clamped onto it, so every load reads a valid row of the item.
+  int wlo = tb, whi = te - 1;
+  int wpage0 = 0;            // first page of the current LDS window
+  auto clampw = [&](int t) { return min(max(t, wlo), whi); };
+
+  // Issue the K/V loads of step s into st (page ids from the LDS window).
+  auto issue = [&](int s, StepRegs<G_::kPieces>& st) {
+    const int t0 = base + s * kStepTokens;
+    const int c0 = clampw(t0 + tau0), c1 = clampw(t0 + tau1);
+    const int pg0 = s_pages[(c0 >> lp) - wpage0];
+    const int pg1 = s_pages[(c1 >> lp) - wpage0];
     const int64_t r0 = ((int64_t)pg0 * a.page_stride + (int64_t)(c0 & page_mask) * a.slot_stride + head_off) * G_::kKvBytes;
     const int64_t r1 = ((int64_t)pg1 * a.page_stride + (int64_t)(c1 & page_mask) * a.slot_stride + head_off) * G_::kKvBytes;
-    // prefetch the page ids of this wave's next step
-    if (step + kWaves < nsteps) {
-      const int tn = t0 + kWaves * kStepTokens;
-      pg0 = pidx[clampt(tn + tau0) >> a.log2_page];
-      pg1 = pidx[clampt(tn + tau1) >> a.log2_page];
-    }
-    u32x4 kr[2][G_::kPieces], vr[2][G_::kPieces];
 #pragma unroll
     for (int p = 0; p < G_::kPieces; ++p) {
-      kr[0][p] = *reinterpret_cast<const u32x4*>(kbase + r0 + 64 * p + 16 * g);
-      kr[1][p] = *reinterpret_cast<const u32x4*>(kbase + r1 + 64 * p + 16 * g);
+      st.k[0][p] = *reinterpret_cast<const u32x4*>(kbase + r0 + 64 * p + 16 * g);
+      st.k[1][p] = *reinterpret_cast<const u32x4*>(kbase + r1 + 64 * p + 16 * g);
     }
 #pragma unroll
     for (int p = 0; p < G_::kPieces; ++p) {
-      vr[0][p] = *reinterpret_cast<const u32x4*>(vbase + r0 + 64 * p + 16 * g);
-      vr[1][p] = *reinterpret_cast<const u32x4*>(vbase + r1 + 64 * p + 16 * g);
+      st.v[0][p] = *reinterpret_cast<const u32x4*>(vbase + r0 + 64 * p + 16 * g);
+      st.v[1][p] = *reinterpret_cast<const u32x4*>(vbase + r1 + 64 * p + 16 * g);
     }
+  };
 
+  // Attend step s whose K/V rows are in st. A step wholly past the window
+  // (the padding step of an odd count) changes nothing and is skipped.
+  auto consume = [&](int s, const StepRegs<G_::kPieces>& st) {
+    const int t0 = base + s * kStepTokens;
+    if (t0 > whi) return;
     // ---- logits: S[tile] rows = tokens, columns = heads
     f32x4 sc[2];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      f32x4 acc_s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < G_::kQkMfma; ++j) {
         v8 kop;
         if constexpr (KV8) {
-          const u32x4 w = kr[tile][j >> 1];
+          const u32x4 w = st.k[tile][j >> 1];
           kop = (j & 1) ? e4m3x8<QBF16>(w[2], w[3]) : e4m3x8<QBF16>(w[0], w[1]);
         } else {
-          kop = __builtin_bit_cast(v8, kr[tile][j]);
+          kop = __builtin_bit_cast(v8, st.k[tile][j]);
         }
-        s = O::mfma(kop, bq[j], s);
+        acc_s = O::mfma(kop, bq[j], acc_s);
       }
-      sc[tile] = s;
+      sc[tile] = acc_s;
     }
-
     // ---- V rows to this wave's LDS copy (row = token within the step)
 #pragma unroll
     for (int p = 0; p < G_::kPieces; ++p) {
-      *reinterpret_cast<u32x4*>(vl + tau0 * G_::kVPitch + 64 * p + 16 * g) = vr[0][p];
-      *reinterpret_cast<u32x4*>(vl + tau1 * G_::kVPitch + 64 * p + 16 * g) = vr[1][p];
+      *reinterpret_cast<u32x4*>(vl + tau0 * G_::kVPitch + 64 * p + 16 * g) = st.v[0][p];
+      *reinterpret_cast<u32x4*>(vl + tau1 * G_::kVPitch + 64 * p + 16 * g) = st.v[1][p];
     }
-
     // ---- online softmax (base 2)
     float x[8];
     float mx = -INFINITY;
@@ -268,7 +314,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
         float v = sc[tile][i] * a.logit_scale;
         if constexpr (CAP) v = a.cap * tanh_from_exp(v * a.inv_cap) * kLog2e;
         const int t = t0 + 8 * g + 4 * tile + i;
-        v = (t >= tb && t < te) ? v : -INFINITY;
+        v = (t >= wlo && t <= whi) ? v : -INFINITY;
         x[4 * tile + i] = v;
         mx = fmaxf(mx, v);
       }
@@ -291,7 +337,6 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
     pw[2] = O::pack(x[4], x[5]);
     pw[3] = O::pack(x[6], x[7]);
     const v8 pop = __builtin_bit_cast(v8, pw);
-
     // ---- O^T += V^T P^T, one MFMA per 16 hd columns
 #pragma unroll
     for (int b = 0; b < G_::kPvMfma; ++b) {
@@ -311,6 +356,52 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
       f32x4 c = acc[b];
       c[0] *= alpha; c[1] *= alpha; c[2] *= alpha; c[3] *= alpha;
       acc[b] = O::mfma(vop, pop, c);
+    }
+  };
+
+  // Steps are processed in windows whose pages fit the LDS page table.
+  // Loads are issued one step ahead and unconditionally (a surplus prefetch
+  // past the window re-reads its last row), which keeps the number of loads
+  // in flight the same on every path, so the compiler's wait before a step
+  // covers that step's loads only.
+  const int win_steps = max(1, ((kPageWin - 1) << lp) >> 5);
+  for (int w0 = 0; w0 < nsteps; w0 += win_steps) {
+    const int w1 = min(nsteps, w0 + win_steps);
+    wlo = max(tb, base + w0 * kStepTokens);
+    whi = min(te, base + w1 * kStepTokens) - 1;
+    wpage0 = wlo >> lp;
+    const int wpages = (whi >> lp) - wpage0 + 1;
+    __syncthreads();                   // previous window fully consumed
+    for (int i = threadIdx.x; i < wpages; i += kWaves * 64) s_pages[i] = pidx[wpage0 + i];
+    __syncthreads();
+    // This wave's steps in the window, taken two at a time; an odd count
+    // gets one more step past the window, which reads clamped rows and whose
+    // tokens are all masked (no effect on the state). The loop body has no
+    // exit in the middle, so each half waits for its own loads only.
+    const int s0 = w0 + ((wave - w0) % kWaves + kWaves) % kWaves;
+    const int mine = s0 < w1 ? (w1 - s0 + kWaves - 1) / kWaves : 0;
+    // The scheduling barriers keep each issue ahead of the step it overlaps:
+    // the loads must leave before the wait for the previous step's rows.
+    if constexpr (G_::kStages == 2) {
+      StepRegs<G_::kPieces> A, B;
+      issue(s0, A);
+      for (int k = 0; k < (mine + 1) / 2; ++k) {
+        const int s = s0 + 2 * k * kWaves;
+        issue(s + kWaves, B);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(s, A);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(s + 2 * kWaves, A);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(s + kWaves, B);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      for (int k = 0; k < mine; ++k) {
+        StepRegs<G_::kPieces> A;
+        issue(s0 + k * kWaves, A);
+        consume(s0 + k * kWaves, A);
+      }
     }
   }
 
@@ -354,12 +445,27 @@ __global__ __launch_bounds__(kWaves * 64) void decode_kernel(DecodeArgs a) {
       if (c == 0) a.ws_lse[(size_t)it.partial * a.num_qo_heads + qh] = lse2;
     }
   }
+  if (threadIdx.x == 0) s_item = next;
+  __syncthreads();                       // LDS free for the next item
+  item = __builtin_amdgcn_readfirstlane(s_item);
+  }
+  // The last workgroup out resets the counters for the next launch: every
+  // other workgroup has already taken its final item number by then.
+  if (threadIdx.x == 0 && atomicAdd(&a.counters[1], 1) == (int)gridDim.x - 1) {
+    atomicExch(&a.counters[0], 0);
+    atomicExch(&a.counters[1], 0);
+  }
 }
 
 // One wavefront per output row: fold the row's states in ascending order.
 // Plan mode: row r is (merge entry r / num_qo_heads, head r % num_qo_heads),
 // states are the entry's workspace slots. Flat mode: row r has num_states
 // states at v[r][k][:], s[r][k].
+//
+// Lanes are split into `cl` chunk lanes x (hd/4) column lanes (float4 each);
+// chunk lane kk folds states kk, kk+cl, ... in ascending order, then the cl
+// partial sums are added in lane order. The sum order depends only on the
+// number of states, so the result is deterministic and batch invariant.
 __global__ __launch_bounds__(kMergeRowsPerBlock * 64) void merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
@@ -391,66 +497,104 @@ __global__ __launch_bounds__(kMergeRowsPerBlock * 64) void merge_kernel(MergeArg
   float M = -INFINITY;
   for (int k = lane; k < nst; k += 64) M = fmaxf(M, ss[k * s_stride] * to2);
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  auto weight = [&](int k) {
+    const float sk = ss[k * s_stride] * to2;
+    return sk == -INFINITY ? 0.0f : fast_exp2(sk - M);
+  };
   float den = 0.0f;
   if (M != -INFINITY) {
-    for (int k = 0; k < nst; ++k) {
-      const float sk = ss[k * s_stride] * to2;
-      den += sk == -INFINITY ? 0.0f : fast_exp2(sk - M);
-    }
+    for (int k = lane; k < nst; k += 64) den += weight(k);
+    for (int off = 1; off < 64; off <<= 1) den += __shfl_xor(den, off);
   }
-  for (int c = lane; c < hd; c += 64) {
-    float num = 0.0f;
-    if (M != -INFINITY) {
-      for (int k = 0; k < nst; ++k) {
-        const float sk = ss[k * s_stride] * to2;
-        const float w = sk == -INFINITY ? 0.0f : fast_exp2(sk - M);
-        num += w * vs[k * v_stride + c];
+  const int ngc = hd >> 2;
+  const bool vec = (hd & 3) == 0 && hd <= 256 && (ngc & (ngc - 1)) == 0 &&
+                   (reinterpret_cast<uintptr_t>(vs) & 15) == 0 && (v_stride & 3) == 0;
+  if (vec) {
+    const int ng = hd >> 2;                  // float4 columns
+    const int cl = 64 / ng;                  // chunk lanes (>= 1)
+    const int cg = lane % ng, kk = lane / ng;
+    f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY && kk < cl) {
+#pragma unroll 8
+      for (int k = kk; k < nst; k += cl) {
+        const float wk = weight(k);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(vs + k * v_stride + 4 * cg);
+        acc4 += wk * x;
       }
     }
-    const float ov = M == -INFINITY ? 0.0f : num / den;
-    const size_t idx = out_row * hd + c;
-    if (a.out_dtype == PKD_F32)
-      reinterpret_cast<float*>(a.v_out)[idx] = ov;
-    else
-      store_out(a.v_out, idx, ov, a.out_dtype == PKD_BF16);
+    // add the chunk lanes' partial sums in lane order
+    for (int off = ng; off < 64; off <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc4[e] += __shfl_xor(acc4[e], off);
+    }
+    if (kk == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float ov = M == -INFINITY ? 0.0f : acc4[e] / den;
+        const size_t idx = out_row * hd + 4 * cg + e;
+        if (a.out_dtype == PKD_F32)
+          reinterpret_cast<float*>(a.v_out)[idx] = ov;
+        else
+          store_out(a.v_out, idx, ov, a.out_dtype == PKD_BF16);
+      }
+    }
+  } else {
+    for (int c = lane; c < hd; c += 64) {
+      float num = 0.0f;
+      if (M != -INFINITY)
+        for (int k = 0; k < nst; ++k) num += weight(k) * vs[k * v_stride + c];
+      const float ov = M == -INFINITY ? 0.0f : num / den;
+      const size_t idx = out_row * hd + c;
+      if (a.out_dtype == PKD_F32)
+        reinterpret_cast<float*>(a.v_out)[idx] = ov;
+      else
+        store_out(a.v_out, idx, ov, a.out_dtype == PKD_BF16);
+    }
   }
   if (a.s_out != nullptr && lane == 0)
     a.s_out[out_row] = M == -INFINITY ? -INFINITY : (M + __builtin_amdgcn_logf(den)) * kLn2;
 }
 
-template <int HD, bool QBF16, bool KV8>
-hipError_t launch_hd(bool cap, const DecodeArgs& a, int32_t items, hipStream_t s) {
-  dim3 grid(items), block(kWaves * 64);
-  if (cap)
-    hipLaunchKernelGGL((decode_kernel<HD, QBF16, KV8, true>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<HD, QBF16, KV8, false>), grid, block, 0, s, a);
-  return hipGetLastError();
+// The kernel instance for (head_dim, q type, KV type, soft cap).
+using DecodeFn = void (*)(DecodeArgs);
+
+template <bool QBF16, bool KV8, bool CAP>
+DecodeFn pick_hd(int hd) {
+  switch (hd) {
+    case 64: return decode_kernel<64, QBF16, KV8, CAP>;
+    case 128: return decode_kernel<128, QBF16, KV8, CAP>;
+    default: return decode_kernel<256, QBF16, KV8, CAP>;
+  }
 }
 
-template <bool QBF16, bool KV8>
-hipError_t launch_types(int hd, bool cap, const DecodeArgs& a, int32_t items, hipStream_t s) {
-  switch (hd) {
-    case 64: return launch_hd<64, QBF16, KV8>(cap, a, items, s);
-    case 128: return launch_hd<128, QBF16, KV8>(cap, a, items, s);
-    default: return launch_hd<256, QBF16, KV8>(cap, a, items, s);
+DecodeFn pick_kernel(const pkd_plan_params& p) {
+  const bool cap = p.logits_soft_cap > 0.0f;
+  const bool qbf = p.q_dtype == PKD_BF16;
+  const bool kv8 = p.kv_dtype == PKD_E4M3;
+  if (qbf) {
+    if (kv8) return cap ? pick_hd<true, true, true>(p.head_dim) : pick_hd<true, true, false>(p.head_dim);
+    return cap ? pick_hd<true, false, true>(p.head_dim) : pick_hd<true, false, false>(p.head_dim);
   }
+  if (kv8) return cap ? pick_hd<false, true, true>(p.head_dim) : pick_hd<false, true, false>(p.head_dim);
+  return cap ? pick_hd<false, false, true>(p.head_dim) : pick_hd<false, false, false>(p.head_dim);
 }
 
 }  // namespace
 
-int launch_decode(const pkd_plan_params& p, const DecodeArgs& a, int32_t items,
+int launch_decode(const pkd_plan_params& p, const DecodeArgs& a, int32_t num_workgroups,
                   void* stream) {
-  if (items <= 0) return hipSuccess;
+  if (num_workgroups <= 0) return hipSuccess;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const bool cap = p.logits_soft_cap > 0.0f;
-  const bool qbf = p.q_dtype == PKD_BF16;
-  const bool kv8 = p.kv_dtype == PKD_E4M3;
-  if (qbf)
-    return kv8 ? launch_types<true, true>(p.head_dim, cap, a, items, s)
-               : launch_types<true, false>(p.head_dim, cap, a, items, s);
-  return kv8 ? launch_types<false, true>(p.head_dim, cap, a, items, s)
-             : launch_types<false, false>(p.head_dim, cap, a, items, s);
+  hipLaunchKernelGGL(pick_kernel(p), dim3(num_workgroups), dim3(kWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+int32_t decode_wgs_per_cu(const pkd_plan_params& p) {
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &blocks, reinterpret_cast<const void*>(pick_kernel(p)), kWaves * 64, 0) != hipSuccess)
+    return 0;
+  return blocks;
 }
 
 int launch_merge(const MergeArgs& a, void* stream) {
@@ -462,3 +606,4 @@ int launch_merge(const MergeArgs& a, void* stream) {
 }
 
 }  // namespace pkd
+

@@ -28,6 +28,8 @@ struct MergeRow {
   int32_t reserved;
 };
 
+// The plan's host copy. The decode workgroups take items in this order from
+// a shared counter.
 struct HostPlan {
   pkd_plan_params params{};
   pkd_plan_info info{};
@@ -42,11 +44,17 @@ void clear_error();
 // Validation of the parameters alone (no page table).
 pkd_status check_params(const pkd_plan_params& p);
 
-// The planner: validates the page table, picks the chunk size and builds the
-// work list and merge list. Pure host code.
+// The planner: validates the page table, picks the chunk size, builds the
+// work units and spreads them over `num_slots` workgroups (the decode
+// workgroups that fit on the GPU at once). Pure host code.
 pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
-                           const int32_t* last_page_len, int32_t num_cus,
+                           const int32_t* last_page_len, int32_t num_slots,
                            HostPlan* out);
+
+// Decode workgroups one compute unit holds at once for these parameters, as
+// built (register and LDS use of the kernel instance); used where the GPU
+// cannot be asked.
+int32_t decode_wgs_per_cu_table(const pkd_plan_params& p);
 
 // Byte offset of the LSE part of the workspace.
 size_t workspace_lse_offset(int32_t num_partials, int32_t num_qo_heads,
@@ -55,6 +63,10 @@ size_t workspace_lse_offset(int32_t num_partials, int32_t num_qo_heads,
 // ----------------------------------------------------------------- kernels
 
 struct DecodeArgs {
+  // counters[0]: next item to take; counters[1]: workgroups finished. Both
+  // are zero when a launch starts; the last workgroup to finish resets them.
+  int32_t* counters;
+  int32_t num_items;
   const void* q;
   const void* k;
   const void* v;
@@ -93,7 +105,10 @@ struct MergeArgs {
 
 // Launch wrappers (decode.hip). Return a hipError_t value as int.
 int launch_decode(const pkd_plan_params& p, const DecodeArgs& a,
-                  int32_t num_items, void* stream);
+                  int32_t num_workgroups, void* stream);
+// Decode workgroups per compute unit reported by the HIP runtime for the
+// kernel instance of `p` (0 on failure).
+int32_t decode_wgs_per_cu(const pkd_plan_params& p);
 int launch_merge(const MergeArgs& a, void* stream);
 
 }  // namespace pkd

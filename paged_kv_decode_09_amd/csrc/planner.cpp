@@ -43,12 +43,20 @@ int64_t chunks_of(const Req& r, int32_t split, int32_t page_size) {
   return last - first + 1;
 }
 
-// Target number of work items when the planner chooses the split: enough
-// workgroups to keep every compute unit busy through the tail.
-constexpr int kItemsPerCu = 8;
-// Smallest chunk the planner creates on its own, in tokens: one step for each
-// wavefront of a workgroup, twice.
-constexpr int kMinChunkTokens = 2 * kWaves * kStepTokens;
+// Work units per workgroup the planner aims for when it chooses the split:
+// enough for the longest-first assignment to even out the workgroups.
+constexpr int kUnitsPerWorkgroup = 4;
+// Units the planner sizes itself are multiples of this many tokens: two steps
+// for each wavefront of a workgroup, so that every wavefront runs an even
+// number of steps (its loop takes steps in pairs).
+constexpr int kUnitQuantum = 2 * kWaves * kStepTokens;
+// Smallest unit the planner creates on its own, in tokens.
+constexpr int kMinUnitTokens = kUnitQuantum;
+// Under a fixed split, chunks longer than this are processed as sub-chunks of
+// this many tokens (cut at fixed offsets from the chunk start), so that the
+// work can be spread over all workgroups. The cut depends only on the
+// request's own length, so results stay batch invariant.
+constexpr int kMaxUnitTokens = 1024;
 
 }  // namespace
 
@@ -111,6 +119,16 @@ pkd_status check_params(const pkd_plan_params& p) {
   return PKD_OK;
 }
 
+int32_t decode_wgs_per_cu_table(const pkd_plan_params& p) {
+  // Register use of the built kernel instances (two steps of K/V rows in
+  // registers): head_dim 256 holds one workgroup of 4 wavefronts per compute
+  // unit, head_dim 128 two (three with E4M3 K/V, which need half the
+  // registers), head_dim 64 four.
+  if (p.head_dim >= 256) return 1;
+  if (p.head_dim == 128) return p.kv_dtype == PKD_E4M3 ? 3 : 2;
+  return 4;
+}
+
 size_t workspace_lse_offset(int32_t num_partials, int32_t num_qo_heads,
                             int32_t head_dim) {
   size_t o_bytes = (size_t)num_partials * num_qo_heads * head_dim * 4;
@@ -118,14 +136,14 @@ size_t workspace_lse_offset(int32_t num_partials, int32_t num_qo_heads,
 }
 
 pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
-                           const int32_t* last_page_len, int32_t num_cus,
+                           const int32_t* last_page_len, int32_t num_slots,
                            HostPlan* out) {
   pkd_status st = check_params(p);
   if (st != PKD_OK) return st;
   const int32_t B = p.batch_size;
   if (B > 0 && (indptr == nullptr || last_page_len == nullptr))
     return fail(PKD_EINVAL, "indptr / last_page_len must not be NULL");
-  if (num_cus < 1) return fail(PKD_EINVAL, fmt("num_cus %d < 1", num_cus));
+  if (num_slots < 1) return fail(PKD_EINVAL, fmt("num_slots %d < 1", num_slots));
   if (B > 0 && indptr[0] != 0)
     return fail(PKD_EINVAL, fmt("indptr[0] = %d, must be 0", indptr[0]));
 
@@ -158,80 +176,101 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
     max_pages = std::max(max_pages, r.pages);
   }
 
-  // ---- split size, in pages (0 = one chunk per request)
+  // ---- chunk size, in pages (0 = one chunk per request), and the largest
+  // unit in tokens.
+  const int64_t slots = std::max<int64_t>(1, num_slots);
   int32_t split = 0;
+  int64_t unit_cap = INT64_MAX;
   if (p.disable_split_kv) {
     split = 0;
   } else if (p.fixed_split_size > 0) {
     split = p.fixed_split_size;
+    unit_cap = std::min<int64_t>((int64_t)split * P, kMaxUnitTokens);
   } else if (B > 0) {
-    const int64_t target = (int64_t)num_cus * kItemsPerCu;
-    auto items_for = [&](int32_t s) {
-      int64_t n = 0;
-      for (const Req& r : reqs) n += chunks_of(r, s, P);
-      return n * p.num_kv_heads;
-    };
-    if (items_for(0) < target) {
-      int32_t lo = std::max(1, (kMinChunkTokens + P - 1) / P);
-      int32_t hi = std::max(lo, max_pages);
-      // smallest split with items <= target (items_for is non-increasing)
-      while (lo < hi) {
-        int32_t mid = lo + (hi - lo) / 2;
-        if (items_for(mid) <= target) hi = mid; else lo = mid + 1;
-      }
-      split = lo >= max_pages ? 0 : lo;
+    const int64_t units_wanted = slots * kUnitsPerWorkgroup;
+    if ((int64_t)B * p.num_kv_heads < units_wanted) {
+      const int64_t total = attended * p.num_kv_heads;
+      int64_t unit = std::max<int64_t>(kMinUnitTokens, (total + units_wanted - 1) / units_wanted);
+      // an even number of steps for every wavefront of the workgroup
+      unit = (unit + kUnitQuantum - 1) / kUnitQuantum * kUnitQuantum;
+      int64_t pages_per_unit = (unit + P - 1) / P;
+      split = pages_per_unit >= max_pages ? 0 : (int32_t)pages_per_unit;
     }
   }
+  if (split > 0 && unit_cap == INT64_MAX) unit_cap = (int64_t)split * P;
 
-  // ---- work items and merge rows
+  // ---- work units: chunks of `split` pages, cut into sub-chunks of at most
+  // unit_cap tokens at offsets from the chunk start
+  struct Unit {
+    pkd_work_item it;
+    int64_t tokens;
+  };
+  std::vector<Unit> units;
   out->params = p;
   out->items.clear();
   out->merges.clear();
   int32_t partials = 0;
   for (int32_t i = 0; i < B; ++i) {
     const Req& r = reqs[i];
-    const int64_t nch = chunks_of(r, split, P);
-    const bool split_req = nch > 1;
-    if (split_req) {
-      if ((int64_t)partials + nch > INT32_MAX)
-        return fail(PKD_EUNSUPPORTED, "too many chunks");
-      out->merges.push_back(MergeRow{i, partials, (int32_t)nch, 0});
-    }
-    const int64_t chunk_tokens = (int64_t)split * P;
-    const int64_t first_chunk = split > 0 ? (r.start / P) / split : 0;
-    for (int64_t c = 0; c < nch; ++c) {
-      int64_t b = split > 0 ? (first_chunk + c) * chunk_tokens : 0;
-      int64_t e = split > 0 ? b + chunk_tokens : r.kv_len;
-      b = std::max<int64_t>(b, r.start);
-      e = std::min<int64_t>(e, r.kv_len);
-      for (int32_t h = 0; h < p.num_kv_heads; ++h) {
-        pkd_work_item it;
-        it.request = i;
-        it.kv_head = h;
-        it.token_begin = (int32_t)b;
-        it.token_end = (int32_t)e;
-        it.page_base = indptr[i];
-        it.partial = split_req ? partials + (int32_t)c : -1;
-        it.chunk = (int32_t)c;
-        it.reserved = 0;
-        out->items.push_back(it);
+    // token ranges of this request's units, in order
+    std::vector<std::pair<int64_t, int64_t>> ranges;
+    if (split <= 0) {
+      ranges.emplace_back(r.start, r.kv_len);
+    } else {
+      const int64_t chunk_tokens = (int64_t)split * P;
+      const int64_t first = (r.start / P) / split;
+      const int64_t nch = chunks_of(r, split, P);
+      for (int64_t c = 0; c < nch; ++c) {
+        const int64_t cb = (first + c) * chunk_tokens;
+        const int64_t ce = std::min<int64_t>(cb + chunk_tokens, r.kv_len);
+        for (int64_t sb = cb; sb < ce; sb += unit_cap) {
+          const int64_t lo = std::max<int64_t>(sb, r.start);
+          const int64_t hi = std::min<int64_t>(sb + unit_cap, ce);
+          if (lo < hi) ranges.emplace_back(lo, hi);
+        }
       }
     }
-    if (split_req) partials += (int32_t)nch;
+    const int64_t n = (int64_t)ranges.size();
+    const bool split_req = n > 1;
+    if (split_req) {
+      if ((int64_t)partials + n > INT32_MAX / 2)
+        return fail(PKD_EUNSUPPORTED, "too many chunks");
+      out->merges.push_back(MergeRow{i, partials, (int32_t)n, 0});
+    }
+    for (int64_t c = 0; c < n; ++c) {
+      for (int32_t h = 0; h < p.num_kv_heads; ++h) {
+        Unit u;
+        u.it.request = i;
+        u.it.kv_head = h;
+        u.it.token_begin = (int32_t)ranges[c].first;
+        u.it.token_end = (int32_t)ranges[c].second;
+        u.it.page_base = indptr[i];
+        u.it.partial = split_req ? partials + (int32_t)c : -1;
+        u.it.chunk = (int32_t)c;
+        u.it.reserved = 0;
+        u.tokens = ranges[c].second - ranges[c].first;
+        units.push_back(u);
+      }
+    }
+    if (split_req) partials += (int32_t)n;
+    if (units.size() > (size_t)(INT32_MAX / 2))
+      return fail(PKD_EUNSUPPORTED, "too many work units");
   }
-  if (out->items.size() > (size_t)INT32_MAX)
-    return fail(PKD_EUNSUPPORTED, "too many work items");
-  // Longest items first so that short ones fill the tail; ties keep the
-  // (request, chunk, kv head) order. The order changes scheduling only: each
-  // item's arithmetic depends on its own token range alone.
-  std::stable_sort(out->items.begin(), out->items.end(),
-                   [](const pkd_work_item& a, const pkd_work_item& b) {
-                     return (a.token_end - a.token_begin) >
-                            (b.token_end - b.token_begin);
-                   });
+
+  // ---- launch order: longest units first. The decode workgroups take
+  // units in this order from a shared counter, so a faster workgroup simply
+  // takes more of them. Only the schedule depends on it: each unit's
+  // arithmetic depends on its own range alone.
+  const int64_t nwg = std::min<int64_t>(slots, (int64_t)units.size());
+  std::stable_sort(units.begin(), units.end(), [](const Unit& a, const Unit& b) {
+    return a.tokens > b.tokens;
+  });
+  out->items.resize(units.size());
+  for (size_t k = 0; k < units.size(); ++k) out->items[k] = units[k].it;
 
   pkd_plan_info& info = out->info;
   info.num_items = (int32_t)out->items.size();
+  info.num_workgroups = (int32_t)nwg;
   info.num_split_requests = (int32_t)out->merges.size();
   info.num_partials = partials;
   info.split_pages = split;

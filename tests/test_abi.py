@@ -32,7 +32,7 @@ def test_library_exports_every_declared_symbol():
 def test_struct_sizes_match_header():
     assert ctypes.sizeof(pkd.pkd_plan_params) == 14 * 4
     assert ctypes.sizeof(pkd.pkd_work_item) == 32
-    assert ctypes.sizeof(pkd.pkd_plan_info) == 32
+    assert ctypes.sizeof(pkd.pkd_plan_info) == 40
 
 
 def query(indptr, last, num_cus=256, **kw):
@@ -84,6 +84,28 @@ def test_run_before_plan_and_bad_merge_args_fail_on_host():
                                 None) == pkd.PKD_OK
 
 
+# Under a fixed split, chunks are processed as units of at most this many
+# tokens, cut at fixed offsets from the chunk start.
+FIXED_UNIT_MAX = 1024
+
+
+def unit_bounds(L, page_size, split, window, cap):
+    """Expected unit ranges: the oracle's chunks (whole requests when split is
+    0), each cut at `cap`-token offsets from the chunk start when a cap
+    applies."""
+    out = []
+    for a, b in oracle.chunk_bounds(L, page_size, split, window):
+        if cap is None:
+            out.append((a, b))
+            continue
+        base = (a // (split * page_size)) * split * page_size if split > 0 else 0
+        for s0 in range(base, b, cap):
+            lo, hi = max(s0, a), min(s0 + cap, b)
+            if lo < hi:
+                out.append((lo, hi))
+    return out
+
+
 def coverage(items, nkv, lengths, starts):
     """Per (request, kv head): the sorted chunk ranges must tile [start, L)."""
     per = {}
@@ -118,18 +140,17 @@ def test_split_chunks_tile_each_request(split, window):
     per = coverage(items, 4, lens, starts)
     if split == 0:
         split = info.split_pages
+        cap = None
     else:
         assert info.split_pages == split
+        cap = FIXED_UNIT_MAX
     for (r, h), ch in per.items():
-        ref = oracle.chunk_bounds(int(lens[r]), 16, split, window)
+        ref = unit_bounds(int(lens[r]), 16, split, window, cap)
         assert [(c[1], c[2]) for c in ch] == ref
     assert info.attended_tokens == sum(int(L) - s for L, s in zip(lens, starts))
-    n_split = sum(1 for L, s in zip(lens, starts)
-                  if len(oracle.chunk_bounds(int(L), 16, split, window)) > 1)
-    assert info.num_split_requests == n_split
-    parts = sum(len(oracle.chunk_bounds(int(L), 16, split, window))
-                for L, s in zip(lens, starts)
-                if len(oracle.chunk_bounds(int(L), 16, split, window)) > 1)
+    nunits = [len(unit_bounds(int(L), 16, split, window, cap)) for L in lens]
+    assert info.num_split_requests == sum(1 for k in nunits if k > 1)
+    parts = sum(k for k in nunits if k > 1)
     assert info.num_partials == parts
     if parts:
         lse_off = (parts * 8 * 128 * 4 + 255) // 256 * 256
@@ -153,14 +174,16 @@ def test_fixed_split_is_batch_invariant():
         assert a == b
 
 
-def test_disable_split_kv_gives_one_chunk_per_request():
+@pytest.mark.parametrize("window", [-1, 777])
+def test_disable_split_kv_gives_one_unit_per_request(window):
     rng = np.random.default_rng(5)
-    lens = rng.integers(1, 100000, 3)
+    lens = np.array(list(rng.integers(1, 100000, 3)) + [1, 255, 256, 257])
     pt = wl.page_table_for(lens, 16, "perm_used", rng)
     info, items = query(pt.indptr, pt.last_page_len, disable_split_kv=True,
-                        window_left=777)
-    assert info.num_items == 3 * 2 and info.workspace_bytes == 0
-    coverage(items, 2, lens, [oracle.window_start(int(L), 777) for L in lens])
+                        window_left=window)
+    assert info.split_pages == 0 and info.workspace_bytes == 0
+    assert info.num_items == len(lens) * 2
+    coverage(items, 2, lens, [oracle.window_start(int(L), window) for L in lens])
 
 
 @pytest.mark.parametrize("name", ["worked_example", "serving_batch",
@@ -177,19 +200,35 @@ def test_named_workload_plans(name):
         fixed_split_size=w.fixed_split_size)
     starts = [oracle.window_start(int(L), w.window_left) for L in pt.lengths]
     coverage(items, w.num_kv_heads, pt.lengths, starts)
-    # longest first
-    sizes = [i.token_end - i.token_begin for i in items]
-    assert sizes == sorted(sizes, reverse=True)
+    assert 1 <= info.num_workgroups <= 256 * 4
     if name == "long_context":
-        assert info.num_items == 640 and info.split_pages == 256
-        assert info.num_partials == 80
-    if name != "long_context":
-        assert info.num_items <= max(8 * 256, w.batch * w.num_kv_heads)
+        # 80 chunks of 256 pages (4096 tokens), each processed as 4 units of
+        # 1024 tokens, for every kv head
+        assert info.split_pages == 256 and info.num_items == 80 * 4 * 8
+        assert info.num_partials == 80 * 4
 
 
-def test_auto_split_respects_minimum_chunk():
+@pytest.mark.parametrize("name", ["serving_batch", "long_context", "gemma2_decode", "fp8_kv"])
+def test_units_are_small_next_to_a_workgroup_share(name):
+    w = wl.WORKLOADS[name]
+    pt = wl.make_page_table(w, np.random.default_rng(w.seed))
+    kw = dict(num_qo_heads=w.num_qo_heads, num_kv_heads=w.num_kv_heads,
+              head_dim=w.head_dim, page_size=w.page_size, window_left=w.window_left,
+              q_data_type=w.q_dtype, kv_data_type=w.kv_dtype,
+              fixed_split_size=w.fixed_split_size)
+    info, items = pkd.plan_query(pt.indptr, pt.last_page_len, 256, **kw)
+    sizes = np.array([i.token_end - i.token_begin for i in items])
+    # taken longest first; the largest unit is small next to a workgroup's
+    # share, so that the shared counter can even out the workgroups
+    assert np.all(np.diff(sizes) <= 0)
+    wgs_per_cu = {64: 4, 128: 3 if w.kv_dtype == "e4m3" else 2, 256: 1}[w.head_dim]
+    assert info.num_workgroups == min(len(items), 256 * wgs_per_cu)
+    assert sizes.max() <= sizes.sum() / info.num_workgroups
+
+
+def test_auto_split_respects_minimum_unit():
     info, items = query([0, 1000], [16], num_qo_heads=64, num_kv_heads=8)
-    assert info.split_pages >= 16
+    assert info.split_pages * 16 >= 256     # two steps for each of 4 waves
     assert all(i.token_end - i.token_begin <= info.split_pages * 16 for i in items)
 
 
