@@ -106,7 +106,7 @@ typedef struct {
   int32_t num_split_requests; /* requests cut into more than one unit       */
   int32_t num_partials;     /* workspace slots (units of split requests)    */
   int32_t split_pages;      /* chunk size in pages; 0 = no split            */
-  int32_t reserved;
+  int32_t workgroups_per_cu; /* decode workgroups resident per compute unit */
   int64_t attended_tokens;  /* sum over requests of attended tokens         */
   size_t workspace_bytes;   /* bytes the workspace of pkd_run must hold     */
 } pkd_plan_info;

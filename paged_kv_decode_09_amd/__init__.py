@@ -59,7 +59,7 @@ class pkd_plan_info(ctypes.Structure):
                 ("num_split_requests", ctypes.c_int32),
                 ("num_partials", ctypes.c_int32),
                 ("split_pages", ctypes.c_int32),
-                ("reserved", ctypes.c_int32),
+                ("workgroups_per_cu", ctypes.c_int32),
                 ("attended_tokens", ctypes.c_int64),
                 ("workspace_bytes", ctypes.c_size_t)]
 

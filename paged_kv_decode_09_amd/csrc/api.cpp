@@ -129,11 +129,15 @@ pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
 
-  const int32_t per_cu = pkd::decode_wgs_per_cu(*params);
+  // Size the launch for the residency the kernel is built for; should the
+  // runtime report less, use that so that no workgroup waits for a slot.
+  const int32_t per_cu = std::min(pkd::decode_wgs_per_cu_table(*params),
+                                  pkd::decode_wgs_per_cu(*params));
   if (per_cu < 1) return pkd::fail(PKD_EHIP, "occupancy query of the decode kernel failed");
   pkd_plan* p = new (std::nothrow) pkd_plan();
   if (p == nullptr) return pkd::fail(PKD_ENOMEM, "plan allocation failed");
   st = pkd::build_host_plan(*params, indptr, last_page_len, cus * per_cu, &p->host);
+  if (st == PKD_OK) p->host.info.workgroups_per_cu = per_cu;
   if (st != PKD_OK) {
     delete p;
     return st;

@@ -136,11 +136,8 @@ struct Geo {
   static constexpr int kPieces = kRowBytes / 64;
   static constexpr int kQkMfma = HD / 32;   // MFMAs per 16-token tile
   static constexpr int kPvMfma = HD / 16;   // MFMAs per 32-token step
-  // Wavefronts per SIMD the register budget is sized for: two steps of K/V
-  // rows live in registers (the next step's loads are issued before the
-  // current step is computed), which leaves room for two wavefronts per SIMD
-  // up to head_dim 128 and one at head_dim 256.
-  static constexpr int kWavesPerSimd = HD == 256 ? 1 : 2;
+  // Steps of K/V rows held in registers: the next step's loads are issued
+  // before the current step is computed.
   static constexpr int kStages = 2;
   // LDS row pitch of the V copy; the pad staggers rows across banks.
   static constexpr int kVPitch = kRowBytes + (KV8 ? 16 : 32);
@@ -186,7 +183,7 @@ struct StepRegs {
 };
 
 template <int HD, bool QBF16, bool KV8, bool CAP>
-__global__ __launch_bounds__(kWaves * 64, HD == 256 ? 1 : 2) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void decode_kernel(DecodeArgs a) {
   using G_ = Geo<HD, KV8>;
   using O = Op<QBF16>;
   using v8 = typename O::v8;

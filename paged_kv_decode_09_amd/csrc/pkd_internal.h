@@ -19,6 +19,15 @@ constexpr int kStepTokens = 32;
 constexpr int kMaxGroup = 16;       // q heads per kv head (one MFMA tile)
 constexpr int kMergeRowsPerBlock = 4;
 
+// Wavefronts per SIMD (= decode workgroups per compute unit) each decode
+// kernel instance is built for: its launch bounds cap its registers to fit,
+// and the planner sizes the launch for it. Two steps of K/V rows stay in
+// registers; head_dim 256 then fits one, head_dim 128 two (three with E4M3
+// K/V rows, half the size), head_dim 64 four.
+constexpr int decode_waves_per_simd(int head_dim, bool kv8) {
+  return head_dim >= 256 ? 1 : head_dim == 128 ? (kv8 ? 3 : 2) : 4;
+}
+
 // One request whose chunks must be merged: its workspace slots are
 // partial_base .. partial_base + num_chunks - 1, in chunk order.
 struct MergeRow {
@@ -51,9 +60,7 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
                            const int32_t* last_page_len, int32_t num_slots,
                            HostPlan* out);
 
-// Decode workgroups one compute unit holds at once for these parameters, as
-// built (register and LDS use of the kernel instance); used where the GPU
-// cannot be asked.
+// Decode workgroups per compute unit the kernel instance of `p` is built for.
 int32_t decode_wgs_per_cu_table(const pkd_plan_params& p);
 
 // Byte offset of the LSE part of the workspace.

@@ -120,13 +120,7 @@ pkd_status check_params(const pkd_plan_params& p) {
 }
 
 int32_t decode_wgs_per_cu_table(const pkd_plan_params& p) {
-  // Register use of the built kernel instances (two steps of K/V rows in
-  // registers): head_dim 256 holds one workgroup of 4 wavefronts per compute
-  // unit, head_dim 128 two (three with E4M3 K/V, which need half the
-  // registers), head_dim 64 four.
-  if (p.head_dim >= 256) return 1;
-  if (p.head_dim == 128) return p.kv_dtype == PKD_E4M3 ? 3 : 2;
-  return 4;
+  return decode_waves_per_simd(p.head_dim, p.kv_dtype == PKD_E4M3);
 }
 
 size_t workspace_lse_offset(int32_t num_partials, int32_t num_qo_heads,
@@ -271,6 +265,7 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
   pkd_plan_info& info = out->info;
   info.num_items = (int32_t)out->items.size();
   info.num_workgroups = (int32_t)nwg;
+  info.workgroups_per_cu = decode_wgs_per_cu_table(p);
   info.num_split_requests = (int32_t)out->merges.size();
   info.num_partials = partials;
   info.split_pages = split;

@@ -221,7 +221,9 @@ def test_units_are_small_next_to_a_workgroup_share(name):
     # taken longest first; the largest unit is small next to a workgroup's
     # share, so that the shared counter can even out the workgroups
     assert np.all(np.diff(sizes) <= 0)
-    wgs_per_cu = {64: 4, 128: 3 if w.kv_dtype == "e4m3" else 2, 256: 1}[w.head_dim]
+    kv8 = w.kv_dtype == "e4m3"
+    wgs_per_cu = {64: 4, 128: 3 if kv8 else 2, 256: 1}[w.head_dim]
+    assert info.workgroups_per_cu == wgs_per_cu
     assert info.num_workgroups == min(len(items), 256 * wgs_per_cu)
     assert sizes.max() <= sizes.sum() / info.num_workgroups
 

@@ -183,7 +183,7 @@ def test_empty_batch_runs_nothing():
     assert o.shape == (0, 8, 128)
 
 
-@pytest.mark.parametrize("hd,kv", [(64, "f16"), (128, "bf16"), (128, "e4m3"), (256, "bf16")])
+@pytest.mark.parametrize("hd,kv", [(64, "f16"), (64, "e4m3"), (128, "bf16"), (128, "e4m3"), (256, "bf16")])
 def test_host_planning_matches_the_device_occupancy(hd, kv):
     """pkd_plan_query (no GPU) must plan the same workgroups as
     pkd_plan_create, whose slot count comes from the HIP runtime."""
@@ -199,5 +199,6 @@ def test_host_planning_matches_the_device_occupancy(hd, kv):
     info, items = pkd.plan_query(pt.indptr, pt.last_page_len, cus, **kw)
     plan = pkd.PagedDecodePlan(pt.indptr, torch.from_numpy(pt.indices).cuda(),
                                pt.last_page_len, **kw)
+    assert plan.info.workgroups_per_cu == info.workgroups_per_cu
     assert plan.info.num_workgroups == info.num_workgroups
     assert plan.info.num_items == info.num_items
