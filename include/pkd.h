@@ -178,8 +178,10 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
 
 /* The two launches of pkd_run, callable separately (same arguments): the
  * decode kernel writes o/lse of unsplit requests and the partial states of
- * split ones; the merge then folds the partials, chunk by chunk in ascending
- * order, into o/lse. pkd_run_merge is a no-op when no request was split. */
+ * split ones; the merge then folds each split request's partials into o/lse
+ * in a summation order fixed by its number of chunks (deterministic and
+ * independent of the batch). pkd_run_merge is a no-op when no request was
+ * split. */
 pkd_status pkd_run_decode(const pkd_plan* plan, const void* q,
                           const void* k_cache, const void* v_cache,
                           int64_t page_stride, float q_scale, float k_scale,
@@ -190,7 +192,10 @@ pkd_status pkd_run_merge(const pkd_plan* plan, void* o, float* lse,
                          void* stream);
 
 /* merge_states (named with fixed_split_size in plan()): combine `num_states`
- * attention states per row by log-sum-exp, in ascending state order.
+ * attention states per row by log-sum-exp:
+ *   M = max_k s[k];  Z = sum_k exp(s[k] - M);  s_out = M + ln Z;
+ *   v_out = sum_k exp(s[k] - s_out) * v[k]
+ * The summation order depends only on num_states (deterministic).
  *   v      device fp32 [rows][num_states][head_dim], per-state normalised o
  *   s      device fp32 [rows][num_states], per-state natural-log LSE;
  *          -inf marks an empty state, which contributes nothing
