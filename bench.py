@@ -2,8 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step is one pkd_run (decode kernel, then merge of split requests) over one
-batch whose inputs already sit in HBM; the plan is built once before timing,
+One step is one pkd_run (one kernel launch: decode, with the merge of split
+requests fused in) over one batch whose inputs already sit in HBM; the plan is built once before timing,
 as plan() is amortised over layers and steps. Successive steps alternate
 between distinct K/V pools so that no step finds the previous step's data in
 the 256 MB Infinity Cache.
@@ -12,8 +12,7 @@ Prints one JSON line. ``value`` is the achieved HBM bandwidth of the whole
 call: algorithmic bytes / wall time per call. Algorithmic bytes = K and V rows
 of the attended tokens (each read once per kv head) + q + o + fp32 lse + the
 page indices of the touched pages + indptr + last_page_len.
-``roofline`` is the decode kernel alone, timed with HIP events on the stream
-it runs on. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample.
+``roofline`` is that kernel, timed with HIP events on the stream it runs on. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample.
 """
 import argparse
 import hashlib
@@ -47,22 +46,23 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, pt, info, split_rows):
-    """(total bytes of one call, bytes of the decode kernel alone)."""
+def algorithmic_bytes(w, pt):
+    """Bytes one call must move: K and V rows of the attended tokens (each
+    read once per kv head), q, o, fp32 lse, the page indices of the touched
+    pages, indptr and last_page_len."""
     B, nq, nkv, hd = w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim
-    kv = info.attended_tokens * nkv * hd * 2 * ELEM[w.kv_dtype]
-    q = B * nq * hd * ELEM[w.q_dtype]
-    out_row = hd * ELEM[w.o_dtype] + 4            # o row + fp32 lse
     ps = w.page_size
-    touched = 0
+    attended, touched = 0, 0
     for i in range(B):
         L = int(pt.lengths[i])
         s0 = 0 if w.window_left < 0 else max(0, L - 1 - w.window_left)
+        attended += L - s0
         touched += (L - 1) // ps - s0 // ps + 1
+    kv = attended * nkv * hd * 2 * ELEM[w.kv_dtype]
+    q = B * nq * hd * ELEM[w.q_dtype]
+    out = B * nq * (hd * ELEM[w.o_dtype] + 4)
     meta = touched * 4 + (B + 1) * 4 + B * 4
-    total = kv + q + B * nq * out_row + meta
-    decode = kv + q + (B - split_rows) * nq * out_row + meta
-    return total, decode
+    return kv + q + out + meta
 
 
 def _sub_pool(case, requests):
@@ -175,8 +175,7 @@ def main():
                       device=dev)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8,
                      device=dev)
-    total_bytes, decode_bytes = algorithmic_bytes(
-        w, case.pt, info, info.num_split_requests)
+    total_bytes = algorithmic_bytes(w, case.pt)
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -189,18 +188,15 @@ def main():
         pool = pools[k % n_pools]
         if evs is not None:
             evs[0].record()
-        plan.run_decode(case.q, pool, k_scale=w.k_scale, v_scale=w.v_scale,
-                        out=o, lse=lse, workspace=ws)
+        plan.run(case.q, pool, k_scale=w.k_scale, v_scale=w.v_scale, out=o,
+                 lse=lse, workspace=ws)
         if evs is not None:
             evs[1].record()
-        plan.run_merge(o, lse, ws)
-        if evs is not None:
-            evs[2].record()
 
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -210,12 +206,11 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     dec_ms = [e[0].elapsed_time(e[1]) for e in events]
-    mrg_ms = [e[1].elapsed_time(e[2]) for e in events]
     dec_avg = float(np.mean(dec_ms))
     value = total_bytes / (ms_step * 1e-3) / 1e9
-    achieved = decode_bytes / (dec_avg * 1e-3) / 1e9
+    achieved = total_bytes / (dec_avg * 1e-3) / 1e9
     src_hash = kernel_source_hash()
-    traffic = profiled_traffic(w.name, src_hash, decode_bytes)
+    traffic = profiled_traffic(w.name, src_hash, total_bytes)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -260,9 +255,8 @@ def main():
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
             "kernel": "decode_kernel",
-            "algorithmic_bytes_per_launch": int(decode_bytes),
+            "algorithmic_bytes_per_launch": int(total_bytes),
             "avg_launch_us": round(dec_avg * 1e3, 2),
-            "merge_avg_us": round(float(np.mean(mrg_ms)) * 1e3, 2),
             "kernel_source_hash": src_hash,
         },
         "cpu_baseline": cpu,

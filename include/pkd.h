@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define PKD_ABI_VERSION 1
+#define PKD_ABI_VERSION 2
 
 typedef enum {
   PKD_OK = 0,
@@ -97,7 +97,7 @@ typedef struct {
   int32_t page_base;        /* indptr[request]                              */
   int32_t partial;          /* -1: writes o/lse; else its workspace slot    */
   int32_t chunk;            /* unit index within the request (ascending)    */
-  int32_t reserved;
+  int32_t num_chunks;       /* units of the request per kv head (1: unsplit) */
 } pkd_work_item;
 
 typedef struct {
@@ -165,31 +165,20 @@ void pkd_plan_destroy(pkd_plan* plan);
  *   workspace, workspace_bytes  device scratch of at least
  *            pkd_plan_info.workspace_bytes (may be NULL when that is 0); its
  *            contents need no initialisation
- * Launches the decode kernel and, if some request was split, the merge.
+ * One kernel launch. Units of a split request write partial states to the
+ * workspace; the workgroup that finishes the last unit of a (request, kv
+ * head) merges that request's partials for the head by log-sum-exp in
+ * ascending chunk order (merge_states named with fixed_split_size), so the
+ * result does not depend on which workgroup ran which unit.
  * Runs of one plan must not overlap in time (for example on two streams):
- * the decode workgroups share a work counter owned by the plan. Runs of
+ * the workgroups share work and merge counters owned by the plan. Runs of
  * different plans may overlap.
- * Errors: PKD_EINVAL (null pointer, page_stride too small),
- * PKD_EWORKSPACE, PKD_EHIP (launch failure). */
+ * Errors: PKD_EINVAL (null pointer, page_stride too small, misaligned
+ * buffer), PKD_EWORKSPACE, PKD_EHIP (launch failure). */
 pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
                    const void* v_cache, int64_t page_stride, float q_scale,
                    float k_scale, float v_scale, void* o, float* lse,
                    void* workspace, size_t workspace_bytes, void* stream);
-
-/* The two launches of pkd_run, callable separately (same arguments): the
- * decode kernel writes o/lse of unsplit requests and the partial states of
- * split ones; the merge then folds each split request's partials into o/lse
- * in a summation order fixed by its number of chunks (deterministic and
- * independent of the batch). pkd_run_merge is a no-op when no request was
- * split. */
-pkd_status pkd_run_decode(const pkd_plan* plan, const void* q,
-                          const void* k_cache, const void* v_cache,
-                          int64_t page_stride, float q_scale, float k_scale,
-                          float v_scale, void* o, float* lse, void* workspace,
-                          size_t workspace_bytes, void* stream);
-pkd_status pkd_run_merge(const pkd_plan* plan, void* o, float* lse,
-                         const void* workspace, size_t workspace_bytes,
-                         void* stream);
 
 /* merge_states (named with fixed_split_size in plan()): combine `num_states`
  * attention states per row by log-sum-exp:

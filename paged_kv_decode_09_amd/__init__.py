@@ -18,6 +18,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkd.so")
+ABI_VERSION = 2            # PKD_ABI_VERSION of include/pkd.h
 
 PKD_OK, PKD_EINVAL, PKD_EUNSUPPORTED, PKD_EHIP, PKD_ENOMEM, PKD_EWORKSPACE = (
     0, -1, -2, -3, -4, -5)
@@ -50,7 +51,7 @@ class pkd_work_item(ctypes.Structure):
     _fields_ = [("request", ctypes.c_int32), ("kv_head", ctypes.c_int32),
                 ("token_begin", ctypes.c_int32), ("token_end", ctypes.c_int32),
                 ("page_base", ctypes.c_int32), ("partial", ctypes.c_int32),
-                ("chunk", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("chunk", ctypes.c_int32), ("num_chunks", ctypes.c_int32)]
 
 
 class pkd_plan_info(ctypes.Structure):
@@ -79,11 +80,6 @@ _SIGS = {
     "pkd_run": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_float,
                                ctypes.c_float, ctypes.c_float, _P, _P, _P,
                                ctypes.c_size_t, _P]),
-    "pkd_run_decode": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64,
-                                      ctypes.c_float, ctypes.c_float,
-                                      ctypes.c_float, _P, _P, _P,
-                                      ctypes.c_size_t, _P]),
-    "pkd_run_merge": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_size_t, _P]),
     "pkd_merge_states": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, _P, ctypes.c_int32, _P,
                                         _P]),
@@ -105,7 +101,7 @@ def lib() -> ctypes.CDLL:
             f = getattr(h, name)
             f.restype = res
             f.argtypes = args
-        if h.pkd_abi_version() != 1:
+        if h.pkd_abi_version() != ABI_VERSION:
             raise ImportError("libpkd.so ABI version mismatch")
         _lib_handle = h
     return _lib_handle
@@ -299,29 +295,6 @@ class PagedDecodePlan:
                              lse.data_ptr() if lse is not None else None,
                              ws_ptr, ws_len, _stream_ptr(stream)))
         return (out, lse) if return_lse else out
-
-    def run_decode(self, q, paged_kv_cache, q_scale=None, k_scale=None,
-                   v_scale=None, out=None, lse=None,
-                   workspace: Optional[torch.Tensor] = None, stream=None):
-        """The decode launch alone (pkd_run_decode)."""
-        (q, kp, vp, stride, sc, out, lse, ws_ptr, ws_len,
-         _ws) = self._args(q, paged_kv_cache, q_scale, k_scale, v_scale, out,
-                           lse, lse is not None, workspace)
-        _check(lib().pkd_run_decode(self._handle, q.data_ptr(), kp, vp, stride,
-                                    sc[0], sc[1], sc[2], out.data_ptr(),
-                                    lse.data_ptr() if lse is not None else None,
-                                    ws_ptr, ws_len, _stream_ptr(stream)))
-        return out, lse
-
-    def run_merge(self, out, lse, workspace, stream=None):
-        """The merge launch alone (pkd_run_merge)."""
-        ws_ptr = workspace.data_ptr() if workspace is not None else None
-        ws_len = workspace.numel() * workspace.element_size() if \
-            workspace is not None else 0
-        _check(lib().pkd_run_merge(self._handle, out.data_ptr(),
-                                   lse.data_ptr() if lse is not None else None,
-                                   ws_ptr, ws_len, _stream_ptr(stream)))
-        return out, lse
 
 
 class BatchDecodeWithPagedKVCacheWrapper:

@@ -2,7 +2,8 @@
 //
 // plan/run split of flashinfer.decode.BatchDecodeWithPagedKVCacheWrapper
 // ("FlashInfer attention kernels" page): plan() does the host work once and
-// uploads the work list; run() only enqueues kernels on the caller's stream.
+// uploads the work list; run() only enqueues one kernel on the caller's
+// stream.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -14,22 +15,28 @@
 struct pkd_plan {
   pkd::HostPlan host;
   const int32_t* indices = nullptr;   // borrowed device pointer
-  void* dev = nullptr;                // items followed by merge rows
+  void* dev = nullptr;                // counters, merge counters, items
   void* staging = nullptr;            // pinned host copy used by the upload
   hipEvent_t uploaded = nullptr;
   int device = 0;
-  // device copy: the decode work counters (zeroed by the upload), the items,
-  // then the merge rows
+  // Device copy, all uploaded from the staging copy (counters as zeros):
+  // the work counters, the per-(request, kv head) merge counters, the items.
   static constexpr size_t kCounterBytes = 64;
+  int32_t merge_stride() const {
+    return 1 + (host.max_units + pkd::kMergeGroup - 1) / pkd::kMergeGroup;
+  }
+  size_t merge_counter_bytes() const {
+    const size_t n =
+        (size_t)host.params.batch_size * host.params.num_kv_heads * merge_stride() * 4;
+    return (n + 63) & ~(size_t)63;
+  }
   int32_t* d_counters() const { return reinterpret_cast<int32_t*>(dev); }
+  int32_t* d_merge_counters() const {
+    return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(dev) + kCounterBytes);
+  }
   const pkd_work_item* d_items() const {
     return reinterpret_cast<const pkd_work_item*>(reinterpret_cast<const char*>(dev) +
-                                                  kCounterBytes);
-  }
-  const pkd::MergeRow* d_merges() const {
-    return reinterpret_cast<const pkd::MergeRow*>(
-        reinterpret_cast<const char*>(d_items()) +
-        host.items.size() * sizeof(pkd_work_item));
+                                                  kCounterBytes + merge_counter_bytes());
   }
 };
 
@@ -50,10 +57,10 @@ void free_plan(pkd_plan* p) {
   delete p;
 }
 
-size_t plan_bytes(const pkd::HostPlan& h) {
-  if (h.items.empty()) return 0;
-  return pkd_plan::kCounterBytes + h.items.size() * sizeof(pkd_work_item) +
-         h.merges.size() * sizeof(pkd::MergeRow);
+size_t plan_bytes(const pkd_plan& p) {
+  if (p.host.items.empty()) return 0;
+  return pkd_plan::kCounterBytes + p.merge_counter_bytes() +
+         p.host.items.size() * sizeof(pkd_work_item);
 }
 
 pkd_status check_run(const pkd_plan* plan, const void* q, const void* k,
@@ -144,7 +151,7 @@ pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
   }
   p->indices = indices;
   p->device = dev;
-  const size_t bytes = plan_bytes(p->host);
+  const size_t bytes = plan_bytes(*p);
   if (bytes > 0) {
     e = hipMalloc(&p->dev, bytes);
     if (e != hipSuccess) {
@@ -159,11 +166,10 @@ pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
                                        hipGetErrorString(e));
     }
     char* s = reinterpret_cast<char*>(p->staging);
-    std::memset(s, 0, pkd_plan::kCounterBytes);
-    s += pkd_plan::kCounterBytes;
-    std::memcpy(s, p->host.items.data(), p->host.items.size() * sizeof(pkd_work_item));
-    s += p->host.items.size() * sizeof(pkd_work_item);
-    std::memcpy(s, p->host.merges.data(), p->host.merges.size() * sizeof(pkd::MergeRow));
+    const size_t zeros = pkd_plan::kCounterBytes + p->merge_counter_bytes();
+    std::memset(s, 0, zeros);
+    std::memcpy(s + zeros, p->host.items.data(),
+                p->host.items.size() * sizeof(pkd_work_item));
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     e = hipMemcpyAsync(p->dev, p->staging, bytes, hipMemcpyHostToDevice, hs);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming);
@@ -188,10 +194,10 @@ pkd_status pkd_plan_get_info(const pkd_plan* plan, pkd_plan_info* info) {
 
 void pkd_plan_destroy(pkd_plan* plan) { free_plan(plan); }
 
-pkd_status pkd_run_decode(const pkd_plan* plan, const void* q, const void* k_cache,
-                          const void* v_cache, int64_t page_stride, float q_scale,
-                          float k_scale, float v_scale, void* o, float* lse,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
+                   const void* v_cache, int64_t page_stride, float q_scale,
+                   float k_scale, float v_scale, void* o, float* lse,
+                   void* workspace, size_t workspace_bytes, void* stream) {
   pkd_status st = check_run(plan, q, k_cache, v_cache, page_stride, o, workspace,
                             workspace_bytes);
   if (st != PKD_OK) return st;
@@ -201,6 +207,8 @@ pkd_status pkd_run_decode(const pkd_plan* plan, const void* q, const void* k_cac
     return pkd::fail(PKD_EINVAL, "q_scale, k_scale and v_scale must be finite");
   pkd::DecodeArgs a{};
   a.counters = plan->d_counters();
+  a.merge_counters = plan->d_merge_counters();
+  a.merge_stride = plan->merge_stride();
   a.num_items = plan->host.info.num_items;
   a.q = q;
   a.k = k_cache;
@@ -224,6 +232,7 @@ pkd_status pkd_run_decode(const pkd_plan* plan, const void* q, const void* k_cac
     a.head_stride = p.page_size * p.head_dim;
   }
   a.num_qo_heads = p.num_qo_heads;
+  a.num_kv_heads = p.num_kv_heads;
   a.group = p.num_qo_heads / p.num_kv_heads;
   int lg = 0;
   while ((1 << lg) < p.page_size) ++lg;
@@ -238,47 +247,6 @@ pkd_status pkd_run_decode(const pkd_plan* plan, const void* q, const void* k_cac
   int e = pkd::launch_decode(p, a, plan->host.info.num_workgroups, stream);
   if (e != hipSuccess) return hip_fail((hipError_t)e, "decode launch");
   return PKD_OK;
-}
-
-pkd_status pkd_run_merge(const pkd_plan* plan, void* o, float* lse,
-                         const void* workspace, size_t workspace_bytes, void* stream) {
-  if (plan == nullptr) return pkd::fail(PKD_EINVAL, "plan is NULL (run before plan)");
-  const pkd_plan_params& p = plan->host.params;
-  const int32_t parts = plan->host.info.num_partials;
-  if (parts == 0) return PKD_OK;
-  if (o == nullptr) return pkd::fail(PKD_EINVAL, "o must not be NULL");
-  if (workspace == nullptr || workspace_bytes < plan->host.info.workspace_bytes)
-    return pkd::fail(PKD_EWORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
-                                         " bytes < required " +
-                                         std::to_string(plan->host.info.workspace_bytes));
-  pkd::MergeArgs m{};
-  m.v = reinterpret_cast<const float*>(workspace);
-  m.s = reinterpret_cast<const float*>(reinterpret_cast<const char*>(workspace) +
-                                       pkd::workspace_lse_offset(parts, p.num_qo_heads,
-                                                                 p.head_dim));
-  m.rows = plan->d_merges();
-  m.v_out = o;
-  m.s_out = lse;
-  m.num_rows = plan->host.info.num_split_requests * p.num_qo_heads;
-  m.num_states = 0;
-  m.head_dim = p.head_dim;
-  m.num_qo_heads = p.num_qo_heads;
-  m.out_dtype = p.o_dtype;
-  m.s_base2 = 1;
-  int e = pkd::launch_merge(m, stream);
-  if (e != hipSuccess) return hip_fail((hipError_t)e, "merge launch");
-  return PKD_OK;
-}
-
-pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
-                   const void* v_cache, int64_t page_stride, float q_scale,
-                   float k_scale, float v_scale, void* o, float* lse,
-                   void* workspace, size_t workspace_bytes, void* stream) {
-  pkd_status st = pkd_run_decode(plan, q, k_cache, v_cache, page_stride, q_scale,
-                                 k_scale, v_scale, o, lse, workspace, workspace_bytes,
-                                 stream);
-  if (st != PKD_OK) return st;
-  return pkd_run_merge(plan, o, lse, workspace, workspace_bytes, stream);
 }
 
 pkd_status pkd_merge_states(const float* v, const float* s, int32_t rows,
@@ -297,15 +265,12 @@ pkd_status pkd_merge_states(const float* v, const float* s, int32_t rows,
   pkd::MergeArgs m{};
   m.v = v;
   m.s = s;
-  m.rows = nullptr;
   m.v_out = v_out;
   m.s_out = s_out;
   m.num_rows = rows;
   m.num_states = num_states;
   m.head_dim = head_dim;
-  m.num_qo_heads = 1;
   m.out_dtype = out_dtype;
-  m.s_base2 = 0;
   int e = pkd::launch_merge(m, stream);
   if (e != hipSuccess) return hip_fail((hipError_t)e, "merge launch");
   return PKD_OK;

@@ -6,8 +6,10 @@
 // chunk of tokens) the G query rows of that kv head attend the chunk's keys and
 // values, found through the CSR page table, with sm_scale, the optional
 // logits_soft_cap (cap*tanh(x/cap)) and the window already folded into the
-// item's token range by the planner. The merge folds per-chunk states by
-// log-sum-exp (the merge_states step named with plan()'s fixed_split_size).
+// item's token range by the planner. Split requests leave per-unit partial
+// states, which the workgroup finishing a (request, kv head)'s last unit
+// folds by log-sum-exp (the merge_states step named with plan()'s
+// fixed_split_size); merge_kernel is the same step as a standalone call.
 //
 // Design (MI355X-first, not the page's):
 //  * One workgroup of 4 wavefronts per work item. Wavefront w takes the
@@ -119,6 +121,27 @@ __device__ __forceinline__ float wave_sum_over_groups(float x) {
   return x;
 }
 
+// Device-scope (agent) relaxed atomic store: it bypasses the caches that are
+// not coherent across the XCDs, so a workgroup on any XCD that loads with
+// the sc1 policy (load_coherent4/1 below) sees the value once the storing
+// wave's store has completed.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Workgroup barrier that orders LDS accesses only. (__syncthreads() also
+// orders global memory, which on this GPU makes every wave first wait for
+// all its loads in flight, including prefetches meant to cross the barrier.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt vmcnt(0): this wave's vector memory operations have completed.
+__device__ __forceinline__ void wait_vector_memory() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 __device__ __forceinline__ void store_out(void* base, size_t idx, float v, int bf16) {
   if (bf16)
     reinterpret_cast<__bf16*>(base)[idx] = (__bf16)v;
@@ -159,27 +182,136 @@ __device__ __forceinline__ int qk_hd(int j, int g) {
   return KV8 ? 64 * (j >> 1) + 16 * g + 8 * (j & 1) : 32 * j + 8 * g;
 }
 
-// The item list is read-only for the whole launch: read it through the
-// constant address space so that it arrives in scalar registers.
-__device__ __forceinline__ pkd_work_item load_item(const pkd_work_item* items, int k) {
-  const __attribute__((address_space(4))) int32_t* w =
-      (const __attribute__((address_space(4))) int32_t*)(items + k);
-  pkd_work_item it;
-  it.request = w[0];
-  it.kv_head = w[1];
-  it.token_begin = w[2];
-  it.token_end = w[3];
-  it.page_base = w[4];
-  it.partial = w[5];
-  it.chunk = w[6];
-  it.reserved = w[7];
-  return it;
-}
-
 template <int NP>
 struct StepRegs {
   u32x4 k[2][NP];
   u32x4 v[2][NP];
+};
+
+// Buffer resource over `bytes` bytes at `base` for the loads below (raw
+// buffer, dword 3 as for every gfx9 raw buffer access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// 16- and 4-byte loads with the sc1 cache policy (device-coherent, the
+// policy of an agent-scope atomic load), up to 16 bytes per instruction.
+constexpr int kCoherentPolicy = 16;   // sc1
+// (The builtins return raw bits as unsigned integers.)
+__device__ __forceinline__ f32x4 load_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherentPolicy));
+}
+__device__ __forceinline__ float load_coherent1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCoherentPolicy));
+}
+
+// merge_states for one (request, kv head) of a split request: fold the G
+// heads' states of `count` workspace slots first, first + stride, ...
+// (normalised outputs, base-2 LSE) by log-sum-exp, strictly in slot order.
+// The result goes to o and the natural-log lse (out_slot < 0), or, as a
+// state of the same form, to workspace slot out_slot (one of the inputs:
+// each thread reads its column of every input before it writes it, and the
+// LSEs are read into LDS before any is written).
+//
+// The LSEs are staged in LDS (`stage`, `stage_floats` floats; if they do not
+// fit, each thread reads them itself, which is only done when the result
+// goes to o). Each thread owns one float4 column of one head and loads the
+// inputs eight at a time, so that eight loads are in flight.
+template <int HD>
+__device__ void merge_partials(const DecodeArgs& a, int request, int qh0, int first, int stride,
+                               int count, int out_slot, float* stage, int stage_floats) {
+  constexpr int kBatch = 8;
+  constexpr int cols4 = HD / 4;
+  const int n = count;
+  const int G = a.group;
+  const int nq = a.num_qo_heads;
+  const size_t span = (size_t)(n - 1) * stride + 1;   // slots covered
+  const __amdgpu_buffer_rsrc_t ro =
+      make_rsrc(a.ws_o + (size_t)first * nq * HD, (uint32_t)(span * nq * HD * 4));
+  const __amdgpu_buffer_rsrc_t rl =
+      make_rsrc(a.ws_lse + (size_t)first * nq, (uint32_t)(span * nq * 4));
+  const bool staged = n * G <= stage_floats;
+  if (staged) {
+    for (int e = threadIdx.x; e < n * G; e += kWaves * 64) {
+      const int k = e / G, h = e - k * G;
+      stage[e] = load_coherent1(rl, (uint32_t)(k * stride * nq + qh0 + h) * 4);
+    }
+  }
+  lds_barrier();
+  for (int e = threadIdx.x; e < G * cols4; e += kWaves * 64) {
+    const int h = e / cols4, c4 = e - h * cols4;
+    auto lse_of = [&](int k) {
+      return staged ? stage[k * G + h]
+                    : load_coherent1(rl, (uint32_t)(k * stride * nq + qh0 + h) * 4);
+    };
+    float M = -INFINITY;
+    for (int k = 0; k < n; ++k) M = fmaxf(M, lse_of(k));
+    float den = 0.0f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+      for (int k0 = 0; k0 < n; k0 += kBatch) {
+        f32x4 x[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int k = min(k0 + j, n - 1);
+          x[j] = load_coherent4(ro, (uint32_t)((k * stride * nq + qh0 + h) * HD + 4 * c4) * 4);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (k0 + j < n) {
+            const float lk = lse_of(k0 + j);
+            const float wk = lk == -INFINITY ? 0.0f : fast_exp2(lk - M);
+            den += wk;
+            num += wk * x[j];
+          }
+        }
+      }
+    }
+    const float lse2 = den > 0.0f ? M + __builtin_amdgcn_logf(den) : -INFINITY;
+    if (out_slot < 0) {
+      const size_t orow = (size_t)request * nq + qh0 + h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        store_out(a.o, orow * HD + 4 * c4 + i, den > 0.0f ? num[i] / den : 0.0f, a.o_bf16);
+      if (a.lse != nullptr && c4 == 0) a.lse[orow] = lse2 * kLn2;
+    } else {
+      float* orow = a.ws_o + ((size_t)out_slot * nq + qh0 + h) * HD + 4 * c4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_coherent(orow + i, den > 0.0f ? num[i] / den : 0.0f);
+      if (c4 == 0) store_coherent(a.ws_lse + (size_t)out_slot * nq + qh0 + h, lse2);
+    }
+  }
+}
+
+// Wave-uniform description of one work item (a pkd_work_item in SGPRs).
+struct Unit {
+  int request, kv_head, tb, te, page_base, partial, chunk, num_chunks;
+};
+
+// Each lane loads dword (lane % 8) of item k: the whole item is then in
+// lanes 0..7 of one VGPR, in flight like any other vector load.
+__device__ __forceinline__ unsigned load_item_lanes(const pkd_work_item* items, int k, int lane) {
+  return reinterpret_cast<const unsigned*>(items + k)[lane & 7];
+}
+__device__ __forceinline__ Unit unit_from_lanes(unsigned v) {
+  Unit u;
+  u.request = __builtin_amdgcn_readlane((int)v, 0);
+  u.kv_head = __builtin_amdgcn_readlane((int)v, 1);
+  u.tb = __builtin_amdgcn_readlane((int)v, 2);
+  u.te = __builtin_amdgcn_readlane((int)v, 3);
+  u.page_base = __builtin_amdgcn_readlane((int)v, 4);
+  u.partial = __builtin_amdgcn_readlane((int)v, 5);
+  u.chunk = __builtin_amdgcn_readlane((int)v, 6);
+  u.num_chunks = __builtin_amdgcn_readlane((int)v, 7);
+  return u;
+}
+
+// One window of a unit's steps: the tokens [wlo, whi] whose pages are in
+// sp[0 ..] (page wpage0 onwards), read for kv head offset head_off.
+struct Win {
+  int base, wlo, whi, wpage0;
+  const int* sp;
+  int64_t head_off;
 };
 
 template <int HD, bool QBF16, bool KV8, bool CAP>
@@ -188,9 +320,11 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   using O = Op<QBF16>;
   using v8 = typename O::v8;
   __shared__ __attribute__((aligned(16))) char smem[kWaves * G_::kWaveLds];
-  __shared__ int s_pages[kPageWin];
+  __shared__ int s_pages[2][kPageWin];   // first window of this unit / of the next
   __shared__ float s_m[kWaves][kMaxGroup];
   __shared__ float s_d[kWaves][kMaxGroup];
+  __shared__ int s_ticket[2];
+  __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
   // wave-uniform (an SGPR), so that the step loop branches on scalars
@@ -198,68 +332,42 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   const int n = lane & 15;        // MFMA row (tile token) / column (q head)
   const int g = lane >> 4;        // lane group
   const int group = a.group;
-  // Work items are taken in order from the plan's counter, one at a time per
-  // workgroup; the next one is requested when the current one starts.
-  __shared__ int s_item;
-  if (threadIdx.x == 0) s_item = atomicAdd(&a.counters[0], 1);
-  __syncthreads();
-  int item = __builtin_amdgcn_readfirstlane(s_item);   // uniform: scalar loads, scalar branches
-  while (item < a.num_items) {
-  // the item list is read-only for the whole launch: scalar loads
-  const pkd_work_item it = load_item(a.items, item);
-  int next = 0;
-  if (threadIdx.x == 0) next = atomicAdd(&a.counters[0], 1);
-  const int tb = it.token_begin, te = it.token_end;
-  const int qh0 = it.kv_head * group;
   const int lp = a.log2_page;
-
-  // ---- q operand: head n of this kv head (zero past G)
-  v8 bq[G_::kQkMfma];
-  {
-    const _Float16* qrow = reinterpret_cast<const _Float16*>(a.q) +
-                           ((size_t)it.request * a.num_qo_heads + qh0 + n) * HD;
-#pragma unroll
-    for (int j = 0; j < G_::kQkMfma; ++j) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (n < group) x = *reinterpret_cast<const u32x4*>(qrow + qk_hd<KV8>(j, g));
-      bq[j] = __builtin_bit_cast(v8, x);
-    }
-  }
-
-  const int base = tb & ~(kStepTokens - 1);
-  const int nsteps = (te - base + kStepTokens - 1) / kStepTokens;
+  const int page_mask = (1 << lp) - 1;
+  const int last_item = a.num_items - 1;
+  // steps per window of pages held in LDS
+  const int win_steps = max(1, ((kPageWin - 1) << lp) >> 5);
   // Token (within a step) whose K row lane n loads for tiles 0 and 1: tile
   // rows 4g'+i then map to tokens 8g'+4*tile+i.
   const int tau0 = 8 * (n >> 2) + (n & 3);
   const int tau1 = tau0 + 4;
-  const int page_mask = (1 << lp) - 1;
-  const int32_t* pidx = a.indices + it.page_base;
-  const int64_t head_off = (int64_t)it.kv_head * a.head_stride;
   const char* kbase = reinterpret_cast<const char*>(a.k);
   const char* vbase = reinterpret_cast<const char*>(a.v);
   char* vl = smem + wave * G_::kWaveLds;
 
-  float m_run = -INFINITY;   // running max (base-2 logits) of head n
-  float d_run = 0.0f;        // this lane's share of the running sum
-  f32x4 acc[G_::kPvMfma];
-#pragma unroll
-  for (int b = 0; b < G_::kPvMfma; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // The first window of a unit: its first win_steps steps.
+  auto first_window = [&](const Unit& u, const int* sp) {
+    Win W;
+    W.base = u.tb & ~(kStepTokens - 1);
+    W.wlo = u.tb;
+    W.whi = min(u.te, W.base + win_steps * kStepTokens) - 1;
+    W.wpage0 = u.tb >> lp;
+    W.sp = sp;
+    W.head_off = (int64_t)u.kv_head * a.head_stride;
+    return W;
+  };
 
-  // Tokens of the current LDS page window are [wlo, whi]; loads of tokens
-  // outside it (masked ones, and the surplus prefetch past the last step) are
-  // clamped onto it, so every load reads a valid row of the item.
-  int wlo = tb, whi = te - 1;
-  int wpage0 = 0;            // first page of the current LDS window
-  auto clampw = [&](int t) { return min(max(t, wlo), whi); };
-
-  // Issue the K/V loads of step s into st (page ids from the LDS window).
-  auto issue = [&](int s, StepRegs<G_::kPieces>& st) {
-    const int t0 = base + s * kStepTokens;
-    const int c0 = clampw(t0 + tau0), c1 = clampw(t0 + tau1);
-    const int pg0 = s_pages[(c0 >> lp) - wpage0];
-    const int pg1 = s_pages[(c1 >> lp) - wpage0];
-    const int64_t r0 = ((int64_t)pg0 * a.page_stride + (int64_t)(c0 & page_mask) * a.slot_stride + head_off) * G_::kKvBytes;
-    const int64_t r1 = ((int64_t)pg1 * a.page_stride + (int64_t)(c1 & page_mask) * a.slot_stride + head_off) * G_::kKvBytes;
+  // Tokens (clamped onto [wlo, whi]) whose rows lane n loads in step s of
+  // window W, for tiles 0 and 1. Tokens outside the window (masked ones, and
+  // the surplus prefetch past its last step) are clamped onto it, so every
+  // load reads a valid row of the unit.
+  auto token = [&](const Win& W, int s, int tau) {
+    return min(max(W.base + s * kStepTokens + tau, W.wlo), W.whi);
+  };
+  // Issue the K/V loads of the rows of tokens c0, c1 (in pages pg0, pg1).
+  auto issue_rows = [&](const Win& W, int c0, int c1, int pg0, int pg1, StepRegs<G_::kPieces>& st) {
+    const int64_t r0 = ((int64_t)pg0 * a.page_stride + (int64_t)(c0 & page_mask) * a.slot_stride + W.head_off) * G_::kKvBytes;
+    const int64_t r1 = ((int64_t)pg1 * a.page_stride + (int64_t)(c1 & page_mask) * a.slot_stride + W.head_off) * G_::kKvBytes;
 #pragma unroll
     for (int p = 0; p < G_::kPieces; ++p) {
       st.k[0][p] = *reinterpret_cast<const u32x4*>(kbase + r0 + 64 * p + 16 * g);
@@ -271,12 +379,33 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
       st.v[1][p] = *reinterpret_cast<const u32x4*>(vbase + r1 + 64 * p + 16 * g);
     }
   };
+  // Issue the K/V loads of step s of window W (page ids from its LDS window).
+  auto issue = [&](const Win& W, int s, StepRegs<G_::kPieces>& st) {
+    const int c0 = token(W, s, tau0), c1 = token(W, s, tau1);
+    issue_rows(W, c0, c1, W.sp[(c0 >> lp) - W.wpage0], W.sp[(c1 >> lp) - W.wpage0], st);
+  };
 
-  // Attend step s whose K/V rows are in st. A step wholly past the window
-  // (the padding step of an odd count) changes nothing and is skipped.
-  auto consume = [&](int s, const StepRegs<G_::kPieces>& st) {
-    const int t0 = base + s * kStepTokens;
-    if (t0 > whi) return;
+  // q operand: head n of the unit's kv head. Columns n >= G load head 0
+  // again: they produce a duplicate of head 0's softmax that stays in its own
+  // columns (no step mixes columns) and is never written out. Every lane
+  // loads, so that the number of loads in flight is the same on every path.
+  v8 bq[G_::kQkMfma];
+  auto load_q = [&](const Unit& u) {
+    const _Float16* qrow = reinterpret_cast<const _Float16*>(a.q) +
+                           ((size_t)u.request * a.num_qo_heads + u.kv_head * group + (n < group ? n : 0)) * HD;
+#pragma unroll
+    for (int j = 0; j < G_::kQkMfma; ++j)
+      bq[j] = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(qrow + qk_hd<KV8>(j, g)));
+  };
+
+  float m_run, d_run;     // running max (base-2 logits) / this lane's sum, head n
+  f32x4 acc[G_::kPvMfma];
+
+  // Attend step s of window W whose K/V rows are in st. A step wholly past
+  // the window (the padding step of an odd count) changes nothing.
+  auto consume = [&](const Win& W, int s, const StepRegs<G_::kPieces>& st) {
+    const int t0 = W.base + s * kStepTokens;
+    if (t0 > W.whi) return;
     // ---- logits: S[tile] rows = tokens, columns = heads
     f32x4 sc[2];
 #pragma unroll
@@ -311,7 +440,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
         float v = sc[tile][i] * a.logit_scale;
         if constexpr (CAP) v = a.cap * tanh_from_exp(v * a.inv_cap) * kLog2e;
         const int t = t0 + 8 * g + 4 * tile + i;
-        v = (t >= wlo && t <= whi) ? v : -INFINITY;
+        v = (t >= W.wlo && t <= W.whi) ? v : -INFINITY;
         x[4 * tile + i] = v;
         mx = fmaxf(mx, v);
       }
@@ -356,146 +485,251 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
     }
   };
 
-  // Steps are processed in windows whose pages fit the LDS page table.
-  // Loads are issued one step ahead and unconditionally (a surplus prefetch
-  // past the window re-reads its last row), which keeps the number of loads
-  // in flight the same on every path, so the compiler's wait before a step
-  // covers that step's loads only.
-  const int win_steps = max(1, ((kPageWin - 1) << lp) >> 5);
-  for (int w0 = 0; w0 < nsteps; w0 += win_steps) {
-    const int w1 = min(nsteps, w0 + win_steps);
-    wlo = max(tb, base + w0 * kStepTokens);
-    whi = min(te, base + w1 * kStepTokens) - 1;
-    wpage0 = wlo >> lp;
-    const int wpages = (whi >> lp) - wpage0 + 1;
-    __syncthreads();                   // previous window fully consumed
-    for (int i = threadIdx.x; i < wpages; i += kWaves * 64) s_pages[i] = pidx[wpage0 + i];
-    __syncthreads();
-    // This wave's steps in the window, taken two at a time; an odd count
-    // gets one more step past the window, which reads clamped rows and whose
-    // tokens are all masked (no effect on the state). The loop body has no
-    // exit in the middle, so each half waits for its own loads only.
-    const int s0 = w0 + ((wave - w0) % kWaves + kWaves) % kWaves;
-    const int mine = s0 < w1 ? (w1 - s0 + kWaves - 1) / kWaves : 0;
-    // The scheduling barriers keep each issue ahead of the step it overlaps:
-    // the loads must leave before the wait for the previous step's rows.
-    if constexpr (G_::kStages == 2) {
-      StepRegs<G_::kPieces> A, B;
-      issue(s0, A);
-      for (int k = 0; k < (mine + 1) / 2; ++k) {
-        const int s = s0 + 2 * k * kWaves;
-        issue(s + kWaves, B);
-        __builtin_amdgcn_sched_barrier(0);
-        consume(s, A);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(s + 2 * kWaves, A);
-        __builtin_amdgcn_sched_barrier(0);
-        consume(s + kWaves, B);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else {
-      for (int k = 0; k < mine; ++k) {
-        StepRegs<G_::kPieces> A;
-        issue(s0 + k * kWaves, A);
-        consume(s0 + k * kWaves, A);
-      }
-    }
+  // ---- Units form a pipeline per workgroup. While unit `cur` is attended,
+  // the item and the page ids of the next unit `nxt` are loaded, and the
+  // last load issue of cur's step loop is nxt's first step, so that cur's
+  // end-of-unit work (wavefront merge, outputs, merge of split requests)
+  // overlaps with those loads. A workgroup holds at most one unit beyond
+  // the current one, plus the ticket it takes while the current one runs.
+  // Its first two units are items blockIdx.x and blockIdx.x + gridDim.x
+  // (the grid never exceeds the item count); later ones are tickets from
+  // the plan's counter, offset by twice the grid size.
+  int cur = blockIdx.x;
+  Unit cu = unit_from_lanes(load_item_lanes(a.items, cur, lane));
+  int nxt = cur + (int)gridDim.x;
+  {
+    const Win W = first_window(cu, s_pages[0]);
+    const int wpages = (W.whi >> lp) - W.wpage0 + 1;
+    const int32_t* pidx = a.indices + cu.page_base;
+    for (int i = threadIdx.x; i < wpages; i += kWaves * 64) s_pages[0][i] = pidx[W.wpage0 + i];
   }
+  lds_barrier();
+  StepRegs<G_::kPieces> A, B;
+  issue(first_window(cu, s_pages[0]), wave, A);
+  load_q(cu);
+  unsigned itemv = load_item_lanes(a.items, min(nxt, last_item), lane);   // item of nxt
+  int buf = 0, par = 0;
 
-  // ---- merge the wavefronts' states in LDS, in wavefront order
-  d_run = wave_sum_over_groups(d_run);
-  __syncthreads();                       // all V copies consumed
-  float* sacc = reinterpret_cast<float*>(vl);   // [16 heads][HD]
-  if (n < group) {
+  while (cur < a.num_items) {
+    // ---- unit start: cur's first step is in flight in A, its q in bq, the
+    // item of nxt in itemv
+    int tk = 0;
+    if (threadIdx.x == 0) tk = atomicAdd(&a.counters[0], 1);   // the unit after nxt
+    // nxt (read after cur's first step): its first page window (the first
+    // kWaves*64 pages now, to LDS at cur's end; more, rarely, then), and the
+    // pages of this wave's first step of nxt (for the hand-over issue)
+    Unit nu;
+    Win Wn;
+    int nwpages, pgn, hpg0, hpg1;
+    const int32_t* npidx;
+    auto load_next = [&]() {
+      nu = unit_from_lanes(itemv);
+      Wn = first_window(nu, s_pages[buf ^ 1]);
+      nwpages = (Wn.whi >> lp) - Wn.wpage0 + 1;
+      npidx = a.indices + nu.page_base;
+      pgn = npidx[Wn.wpage0 + min((int)threadIdx.x, nwpages - 1)];
+      hpg0 = npidx[token(Wn, wave, tau0) >> lp];
+      hpg1 = npidx[token(Wn, wave, tau1) >> lp];
+    };
+
+    m_run = -INFINITY;
+    d_run = 0.0f;
 #pragma unroll
-    for (int b = 0; b < G_::kPvMfma; ++b)
+    for (int b = 0; b < G_::kPvMfma; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const int base = cu.tb & ~(kStepTokens - 1);
+    const int nsteps = (cu.te - base + kStepTokens - 1) / kStepTokens;
+    const int qh0 = cu.kv_head * group;
+
+    // Steps are processed in windows whose pages fit the LDS page table. A
+    // wave takes every kWaves-th step of a window, one step ahead of the
+    // loads (buffers A and B alternate); the count is padded to an even
+    // number >= 4 with steps past the window, which read clamped rows and
+    // whose tokens are all masked (no effect on the state). The first and
+    // the last half-step are peeled and the loop body runs at least once,
+    // so that the same loads are in flight on every path through it and the
+    // compiler's wait before a step covers that step's loads only. The last
+    // issue of the last window is the next unit's first step.
+    int w0 = 0;
+    do {
+      const int w1 = min(nsteps, w0 + win_steps);
+      Win W;
+      W.base = base;
+      W.wlo = max(cu.tb, base + w0 * kStepTokens);
+      W.whi = min(cu.te, base + w1 * kStepTokens) - 1;
+      W.wpage0 = W.wlo >> lp;
+      W.sp = s_pages[buf];
+      W.head_off = (int64_t)cu.kv_head * a.head_stride;
+      const int s0 = w0 + ((wave - w0) % kWaves + kWaves) % kWaves;
+      const int mine = s0 < w1 ? (w1 - s0 + kWaves - 1) / kWaves : 0;
+      const int m2 = max(4, (mine + 1) & ~1);
+      if (w0 > 0) {
+        // a later window: its pages replace the previous window's
+        lds_barrier();
+        const int wpages = (W.whi >> lp) - W.wpage0 + 1;
+        const int32_t* pidx = a.indices + cu.page_base;
+        for (int i = threadIdx.x; i < wpages; i += kWaves * 64) s_pages[buf][i] = pidx[W.wpage0 + i];
+        lds_barrier();
+        issue(W, s0, A);
+      }
+      // The scheduling barriers keep each issue ahead of the step it overlaps:
+      // the loads must leave before the wait for the previous step's rows.
+      issue(W, s0 + kWaves, B);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(W, s0, A);
+      __builtin_amdgcn_sched_barrier(0);
+      load_next();                       // again (same loads) in a later window
+      __builtin_amdgcn_sched_barrier(0);
+      int j = 1;
+      do {
+        issue(W, s0 + (j + 1) * kWaves, A);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(W, s0 + j * kWaves, B);
+        __builtin_amdgcn_sched_barrier(0);
+        issue(W, s0 + (j + 2) * kWaves, B);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(W, s0 + (j + 1) * kWaves, A);
+        __builtin_amdgcn_sched_barrier(0);
+        j += 2;
+      } while (j + 1 < m2);
+      {
+        // last issue: the next unit's first step after the last window,
+        // else a clamped surplus step of this window
+        const bool hand = w1 == nsteps;
+        const int c0 = token(W, s0 + m2 * kWaves, tau0);
+        const int c1 = token(W, s0 + m2 * kWaves, tau1);
+        const int pg0 = W.sp[(c0 >> lp) - W.wpage0];
+        const int pg1 = W.sp[(c1 >> lp) - W.wpage0];
+        issue_rows(hand ? Wn : W, hand ? token(Wn, wave, tau0) : c0,
+                   hand ? token(Wn, wave, tau1) : c1, hand ? hpg0 : pg0, hand ? hpg1 : pg1, A);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      consume(W, s0 + (m2 - 1) * kWaves, B);
+      __builtin_amdgcn_sched_barrier(0);
+      w0 = w1;
+    } while (w0 < nsteps);
+
+    // ---- end of cur: nxt's pages and the ticket, this wave's state to LDS
+    if ((int)threadIdx.x < nwpages) s_pages[buf ^ 1][threadIdx.x] = pgn;
+    for (int i = threadIdx.x + kWaves * 64; i < nwpages; i += kWaves * 64)
+      s_pages[buf ^ 1][i] = npidx[Wn.wpage0 + i];
+    if (threadIdx.x == 0) s_ticket[par] = 2 * (int)gridDim.x + tk;
+    d_run = wave_sum_over_groups(d_run);
+    float* sacc = reinterpret_cast<float*>(vl);   // [16 heads][HD], own region
+    if (n < group) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sacc[n * HD + 16 * b + 4 * g + i] = acc[b][i];
-    if (g == 0) {
-      s_m[wave][n] = m_run;
-      s_d[wave][n] = d_run;
+      for (int b = 0; b < G_::kPvMfma; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[n * HD + 16 * b + 4 * g + i] = acc[b][i];
+      if (g == 0) {
+        s_m[wave][n] = m_run;
+        s_d[wave][n] = d_run;
+      }
     }
-  }
-  __syncthreads();
-  const int total = group * HD;
-  for (int e = threadIdx.x; e < total; e += kWaves * 64) {
-    const int h = e / HD, c = e - h * HD;
-    float M = s_m[0][h];
+    lds_barrier();
+    // the unit after nxt: its item, to be read during nxt
+    const int nxt2 = __builtin_amdgcn_readfirstlane(s_ticket[par]);
+    // ---- merge the wavefronts' states, in wavefront order
+    const int total = group * HD;
+    for (int e = threadIdx.x; e < total; e += kWaves * 64) {
+      const int h = e / HD, c = e - h * HD;
+      float M = s_m[0][h];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-    float num = 0.0f, den = 0.0f;
+      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+      float num = 0.0f, den = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = s_m[w][h];
-      const float sw = mw == -INFINITY ? 0.0f : fast_exp2(mw - M);
-      num += sw * reinterpret_cast<const float*>(smem + w * G_::kWaveLds)[h * HD + c];
-      den += sw * s_d[w][h];
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = s_m[w][h];
+        const float sw = mw == -INFINITY ? 0.0f : fast_exp2(mw - M);
+        num += sw * reinterpret_cast<const float*>(smem + w * G_::kWaveLds)[h * HD + c];
+        den += sw * s_d[w][h];
+      }
+      const float ov = num / den * a.v_scale;
+      const float lse2 = M + __builtin_amdgcn_logf(den);
+      const int qh = qh0 + h;
+      if (cu.partial < 0) {
+        store_out(a.o, ((size_t)cu.request * a.num_qo_heads + qh) * HD + c, ov, a.o_bf16);
+        if (a.lse != nullptr && c == 0) a.lse[(size_t)cu.request * a.num_qo_heads + qh] = lse2 * kLn2;
+      } else {
+        // device-coherent stores: the merging workgroup may sit on another XCD
+        store_coherent(a.ws_o + ((size_t)cu.partial * a.num_qo_heads + qh) * HD + c, ov);
+        if (c == 0) store_coherent(a.ws_lse + (size_t)cu.partial * a.num_qo_heads + qh, lse2);
+      }
     }
-    const float ov = num / den * a.v_scale;
-    const float lse2 = M + __builtin_amdgcn_logf(den);
-    const int qh = qh0 + h;
-    if (it.partial < 0) {
-      store_out(a.o, ((size_t)it.request * a.num_qo_heads + qh) * HD + c, ov, a.o_bf16);
-      if (a.lse != nullptr && c == 0) a.lse[(size_t)it.request * a.num_qo_heads + qh] = lse2 * kLn2;
-    } else {
-      a.ws_o[((size_t)it.partial * a.num_qo_heads + qh) * HD + c] = ov;
-      if (c == 0) a.ws_lse[(size_t)it.partial * a.num_qo_heads + qh] = lse2;
+    if (cu.partial >= 0) {
+      // Count this unit once its partial state has reached the device-coherent
+      // level. Units are merged in runs of kMergeGroup consecutive units, then
+      // the runs: the workgroup that counts the last unit of a run merges the
+      // run into the run's first slot (or straight into o if the request has
+      // a single run), and the one that counts the last run merges the runs.
+      // Which workgroups these are does not change the result.
+      wait_vector_memory();
+      lds_barrier();
+      const int n = cu.num_chunks;
+      const int run = cu.chunk / kMergeGroup;
+      const int runs = (n + kMergeGroup - 1) / kMergeGroup;
+      const int run_len = min(kMergeGroup, n - run * kMergeGroup);
+      const int slot0 = cu.partial - cu.chunk;
+      int32_t* cnt = a.merge_counters +
+                     ((size_t)cu.request * a.num_kv_heads + cu.kv_head) * a.merge_stride;
+      float* stage = reinterpret_cast<float*>(smem);
+      const int stage_floats = kWaves * G_::kWaveLds / 4;
+      if (threadIdx.x == 0) s_last = atomicAdd(cnt + 1 + run, 1) == run_len - 1;
+      lds_barrier();
+      if (__builtin_amdgcn_readfirstlane(s_last)) {
+        const int rslot = slot0 + run * kMergeGroup;
+        merge_partials<HD>(a, cu.request, qh0, rslot, 1, run_len, runs == 1 ? -1 : rslot,
+                           stage, stage_floats);
+        if (threadIdx.x == 0) atomicExch(cnt + 1 + run, 0);   // ready for the next launch
+        if (runs > 1) {
+          wait_vector_memory();
+          lds_barrier();
+          if (threadIdx.x == 0) s_last = atomicAdd(cnt, 1) == runs - 1;
+          lds_barrier();
+          if (__builtin_amdgcn_readfirstlane(s_last)) {
+            merge_partials<HD>(a, cu.request, qh0, slot0, kMergeGroup, runs, -1, stage,
+                               stage_floats);
+            if (threadIdx.x == 0) atomicExch(cnt, 0);
+          }
+        }
+      }
     }
-  }
-  if (threadIdx.x == 0) s_item = next;
-  __syncthreads();                       // LDS free for the next item
-  item = __builtin_amdgcn_readfirstlane(s_item);
+    load_q(nu);
+    itemv = load_item_lanes(a.items, min(nxt2, last_item), lane);
+    lds_barrier();                       // LDS free for the next unit
+    cur = nxt;
+    cu = nu;
+    nxt = nxt2;
+    par ^= 1;
+    buf ^= 1;
   }
   // The last workgroup out resets the counters for the next launch: every
-  // other workgroup has already taken its final item number by then.
+  // other workgroup has already taken its final ticket by then.
   if (threadIdx.x == 0 && atomicAdd(&a.counters[1], 1) == (int)gridDim.x - 1) {
     atomicExch(&a.counters[0], 0);
     atomicExch(&a.counters[1], 0);
   }
 }
 
-// One wavefront per output row: fold the row's states in ascending order.
-// Plan mode: row r is (merge entry r / num_qo_heads, head r % num_qo_heads),
-// states are the entry's workspace slots. Flat mode: row r has num_states
-// states at v[r][k][:], s[r][k].
+// merge_states: one wavefront per row folds the row's num_states states
+// (v[row][k][:], s[row][k], natural-log LSE).
 //
 // Lanes are split into `cl` chunk lanes x (hd/4) column lanes (float4 each);
 // chunk lane kk folds states kk, kk+cl, ... in ascending order, then the cl
-// partial sums are added in lane order. The sum order depends only on the
-// number of states, so the result is deterministic and batch invariant.
+// partial sums are added in a fixed butterfly. The sum order depends only on
+// num_states, so the result is deterministic.
 __global__ __launch_bounds__(kMergeRowsPerBlock * 64) void merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * kMergeRowsPerBlock + (threadIdx.x >> 6);
   if (row >= a.num_rows) return;
   const int hd = a.head_dim;
-  const float* vs;
-  const float* ss;
-  int64_t v_stride, s_stride;   // between consecutive states
-  int nst;
-  size_t out_row;
-  if (a.rows != nullptr) {
-    const MergeRow mr = a.rows[row / a.num_qo_heads];
-    const int qh = row % a.num_qo_heads;
-    nst = mr.num_chunks;
-    vs = a.v + ((size_t)mr.partial_base * a.num_qo_heads + qh) * hd;
-    ss = a.s + (size_t)mr.partial_base * a.num_qo_heads + qh;
-    v_stride = (int64_t)a.num_qo_heads * hd;
-    s_stride = a.num_qo_heads;
-    out_row = (size_t)mr.request * a.num_qo_heads + qh;
-  } else {
-    nst = a.num_states;
-    vs = a.v + (size_t)row * nst * hd;
-    ss = a.s + (size_t)row * nst;
-    v_stride = hd;
-    s_stride = 1;
-    out_row = row;
-  }
-  const float to2 = a.s_base2 ? 1.0f : kLog2e;
+  const int nst = a.num_states;
+  const float* vs = a.v + (size_t)row * nst * hd;
+  const float* ss = a.s + (size_t)row * nst;
   float M = -INFINITY;
-  for (int k = lane; k < nst; k += 64) M = fmaxf(M, ss[k * s_stride] * to2);
+  for (int k = lane; k < nst; k += 64) M = fmaxf(M, ss[k] * kLog2e);
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   auto weight = [&](int k) {
-    const float sk = ss[k * s_stride] * to2;
+    const float sk = ss[k] * kLog2e;
     return sk == -INFINITY ? 0.0f : fast_exp2(sk - M);
   };
   float den = 0.0f;
@@ -503,11 +737,16 @@ __global__ __launch_bounds__(kMergeRowsPerBlock * 64) void merge_kernel(MergeArg
     for (int k = lane; k < nst; k += 64) den += weight(k);
     for (int off = 1; off < 64; off <<= 1) den += __shfl_xor(den, off);
   }
-  const int ngc = hd >> 2;
-  const bool vec = (hd & 3) == 0 && hd <= 256 && (ngc & (ngc - 1)) == 0 &&
-                   (reinterpret_cast<uintptr_t>(vs) & 15) == 0 && (v_stride & 3) == 0;
+  auto put = [&](size_t idx, float ov) {
+    if (a.out_dtype == PKD_F32)
+      reinterpret_cast<float*>(a.v_out)[idx] = ov;
+    else
+      store_out(a.v_out, idx, ov, a.out_dtype == PKD_BF16);
+  };
+  const int ng = hd >> 2;                    // float4 columns
+  const bool vec = (hd & 3) == 0 && hd <= 256 && (ng & (ng - 1)) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.v) & 15) == 0;
   if (vec) {
-    const int ng = hd >> 2;                  // float4 columns
     const int cl = 64 / ng;                  // chunk lanes (>= 1)
     const int cg = lane % ng, kk = lane / ng;
     f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
@@ -515,41 +754,29 @@ __global__ __launch_bounds__(kMergeRowsPerBlock * 64) void merge_kernel(MergeArg
 #pragma unroll 8
       for (int k = kk; k < nst; k += cl) {
         const float wk = weight(k);
-        const f32x4 x = *reinterpret_cast<const f32x4*>(vs + k * v_stride + 4 * cg);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(vs + (size_t)k * hd + 4 * cg);
         acc4 += wk * x;
       }
     }
-    // add the chunk lanes' partial sums in lane order
     for (int off = ng; off < 64; off <<= 1) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc4[e] += __shfl_xor(acc4[e], off);
     }
     if (kk == 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float ov = M == -INFINITY ? 0.0f : acc4[e] / den;
-        const size_t idx = out_row * hd + 4 * cg + e;
-        if (a.out_dtype == PKD_F32)
-          reinterpret_cast<float*>(a.v_out)[idx] = ov;
-        else
-          store_out(a.v_out, idx, ov, a.out_dtype == PKD_BF16);
-      }
+      for (int e = 0; e < 4; ++e)
+        put((size_t)row * hd + 4 * cg + e, M == -INFINITY ? 0.0f : acc4[e] / den);
     }
   } else {
     for (int c = lane; c < hd; c += 64) {
       float num = 0.0f;
       if (M != -INFINITY)
-        for (int k = 0; k < nst; ++k) num += weight(k) * vs[k * v_stride + c];
-      const float ov = M == -INFINITY ? 0.0f : num / den;
-      const size_t idx = out_row * hd + c;
-      if (a.out_dtype == PKD_F32)
-        reinterpret_cast<float*>(a.v_out)[idx] = ov;
-      else
-        store_out(a.v_out, idx, ov, a.out_dtype == PKD_BF16);
+        for (int k = 0; k < nst; ++k) num += weight(k) * vs[(size_t)k * hd + c];
+      put((size_t)row * hd + c, M == -INFINITY ? 0.0f : num / den);
     }
   }
   if (a.s_out != nullptr && lane == 0)
-    a.s_out[out_row] = M == -INFINITY ? -INFINITY : (M + __builtin_amdgcn_logf(den)) * kLn2;
+    a.s_out[row] = M == -INFINITY ? -INFINITY : (M + __builtin_amdgcn_logf(den)) * kLn2;
 }
 
 // The kernel instance for (head_dim, q type, KV type, soft cap).

@@ -18,18 +18,22 @@ constexpr int kWaves = 4;
 constexpr int kStepTokens = 32;
 constexpr int kMaxGroup = 16;       // q heads per kv head (one MFMA tile)
 constexpr int kMergeRowsPerBlock = 4;
+// Units of a split request are merged in two levels: each run of
+// kMergeGroup consecutive units of a (request, kv head) first, then the runs.
+constexpr int kMergeGroup = 8;
 
 // Wavefronts per SIMD (= decode workgroups per compute unit) each decode
 // kernel instance is built for: its launch bounds cap its registers to fit,
-// and the planner sizes the launch for it. Two steps of K/V rows stay in
-// registers; head_dim 256 then fits one, head_dim 128 two (three with E4M3
-// K/V rows, half the size), head_dim 64 four.
+// and the planner sizes the launch for it. Two steps of K/V rows, the next
+// unit's page ids and the running state stay in registers without spilling
+// (a spill reload would wait for every load in flight): one wavefront per
+// SIMD at head_dim 256, two at 128, three at 64.
 constexpr int decode_waves_per_simd(int head_dim, bool kv8) {
-  return head_dim >= 256 ? 1 : head_dim == 128 ? (kv8 ? 3 : 2) : 4;
+  return (void)kv8, head_dim >= 256 ? 1 : head_dim == 128 ? 2 : 3;
 }
 
-// One request whose chunks must be merged: its workspace slots are
-// partial_base .. partial_base + num_chunks - 1, in chunk order.
+// One split request: its workspace slots are partial_base ..
+// partial_base + num_chunks - 1, in chunk order.
 struct MergeRow {
   int32_t request;
   int32_t partial_base;
@@ -42,6 +46,7 @@ struct MergeRow {
 struct HostPlan {
   pkd_plan_params params{};
   pkd_plan_info info{};
+  int32_t max_units = 0;   // most units of one request (per kv head)
   std::vector<pkd_work_item> items;
   std::vector<MergeRow> merges;
 };
@@ -73,6 +78,11 @@ struct DecodeArgs {
   // counters[0]: next item to take; counters[1]: workgroups finished. Both
   // are zero when a launch starts; the last workgroup to finish resets them.
   int32_t* counters;
+  // [B][num_kv_heads][merge_stride] per (request, kv head) of a split
+  // request: [0] runs merged, [1 + r] units of run r finished. Zero when a
+  // launch starts; each is reset by the workgroup that completes it.
+  int32_t* merge_counters;
+  int32_t merge_stride;
   int32_t num_items;
   const void* q;
   const void* k;
@@ -87,6 +97,7 @@ struct DecodeArgs {
   int32_t slot_stride;  // elements between tokens of a page
   int32_t head_stride;  // elements between kv heads of a page
   int32_t num_qo_heads;
+  int32_t num_kv_heads;
   int32_t group;        // G
   int32_t log2_page;
   int32_t o_bf16;       // output dtype: 0 = f16, 1 = bf16
@@ -97,17 +108,14 @@ struct DecodeArgs {
 };
 
 struct MergeArgs {
-  const float* v;       // per-state outputs
-  const float* s;       // per-state LSE
-  const MergeRow* rows; // plan merge list (plan mode) or NULL (flat mode)
+  const float* v;       // [num_rows][num_states][head_dim] per-state outputs
+  const float* s;       // [num_rows][num_states] per-state natural-log LSE
   void* v_out;
   float* s_out;
-  int32_t num_rows;     // rows to produce
-  int32_t num_states;   // flat mode: states per row
+  int32_t num_rows;
+  int32_t num_states;
   int32_t head_dim;
-  int32_t num_qo_heads; // plan mode: heads per request
   int32_t out_dtype;    // pkd_dtype of v_out
-  int32_t s_base2;      // 1: s is log2-based (plan workspace); 0: natural
 };
 
 // Launch wrappers (decode.hip). Return a hipError_t value as int.

@@ -203,6 +203,7 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
   out->params = p;
   out->items.clear();
   out->merges.clear();
+  out->max_units = 0;
   int32_t partials = 0;
   for (int32_t i = 0; i < B; ++i) {
     const Req& r = reqs[i];
@@ -226,6 +227,7 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
     }
     const int64_t n = (int64_t)ranges.size();
     const bool split_req = n > 1;
+    out->max_units = std::max<int32_t>(out->max_units, (int32_t)n);
     if (split_req) {
       if ((int64_t)partials + n > INT32_MAX / 2)
         return fail(PKD_EUNSUPPORTED, "too many chunks");
@@ -241,7 +243,7 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
         u.it.page_base = indptr[i];
         u.it.partial = split_req ? partials + (int32_t)c : -1;
         u.it.chunk = (int32_t)c;
-        u.it.reserved = 0;
+        u.it.num_chunks = (int32_t)n;
         u.tokens = ranges[c].second - ranges[c].first;
         units.push_back(u);
       }
@@ -256,12 +258,20 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
   // takes more of them. Only the schedule depends on it: each unit's
   // arithmetic depends on its own range alone.
   const int64_t nwg = std::min<int64_t>(slots, (int64_t)units.size());
+  // Among equal lengths, requests with more units go first: the last unit of
+  // a split request merges all of them, and the short merges then come last.
   std::stable_sort(units.begin(), units.end(), [](const Unit& a, const Unit& b) {
-    return a.tokens > b.tokens;
+    if (a.tokens != b.tokens) return a.tokens > b.tokens;
+    return a.it.num_chunks > b.it.num_chunks;
   });
   out->items.resize(units.size());
   for (size_t k = 0; k < units.size(); ++k) out->items[k] = units[k].it;
 
+  // the merge addresses one request's partial states with 32-bit offsets
+  if ((int64_t)partials * p.num_qo_heads * p.head_dim * 4 > INT32_MAX)
+    return fail(PKD_EUNSUPPORTED, fmt("%d partial states of %d heads x %d exceed the "
+                                      "2 GiB workspace limit",
+                                      partials, p.num_qo_heads, p.head_dim));
   pkd_plan_info& info = out->info;
   info.num_items = (int32_t)out->items.size();
   info.num_workgroups = (int32_t)nwg;

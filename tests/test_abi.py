@@ -23,10 +23,10 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     lib = pkd.lib()
     names = header_functions()
-    assert len(names) >= 10
+    assert len(names) == 8
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.pkd_abi_version() == 1
+    assert lib.pkd_abi_version() == pkd.ABI_VERSION == 2
 
 
 def test_struct_sizes_match_header():
@@ -72,8 +72,6 @@ def test_run_before_plan_and_bad_merge_args_fail_on_host():
     st = lib.pkd_run(None, None, None, None, 0, 1.0, 1.0, 1.0, None, None,
                      None, 0, None)
     assert st == pkd.PKD_EINVAL and b"before plan" in lib.pkd_last_error()
-    st = lib.pkd_run_merge(None, None, None, None, 0, None)
-    assert st == pkd.PKD_EINVAL
     st = lib.pkd_merge_states(None, None, 4, 2, 0, None, pkd.PKD_F32, None, None)
     assert st == pkd.PKD_EUNSUPPORTED
     st = lib.pkd_merge_states(None, None, 4, 2, 64, None, 7, None, None)
@@ -222,7 +220,7 @@ def test_units_are_small_next_to_a_workgroup_share(name):
     # share, so that the shared counter can even out the workgroups
     assert np.all(np.diff(sizes) <= 0)
     kv8 = w.kv_dtype == "e4m3"
-    wgs_per_cu = {64: 4, 128: 3 if kv8 else 2, 256: 1}[w.head_dim]
+    wgs_per_cu = {64: 3, 128: 2, 256: 1}[w.head_dim]
     assert info.workgroups_per_cu == wgs_per_cu
     assert info.num_workgroups == min(len(items), 256 * wgs_per_cu)
     assert sizes.max() <= sizes.sum() / info.num_workgroups
