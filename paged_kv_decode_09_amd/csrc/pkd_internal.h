@@ -26,10 +26,13 @@ constexpr int kMergeGroup = 8;
 // kernel instance is built for: its launch bounds cap its registers to fit,
 // and the planner sizes the launch for it. Two steps of K/V rows, the next
 // unit's page ids and the running state stay in registers without spilling
-// (a spill reload would wait for every load in flight): one wavefront per
-// SIMD at head_dim 256, two at 128, three at 64.
+// (a spill reload would wait for every load in flight). One workgroup per
+// compute unit already keeps several times the loads in flight that HBM
+// needs to stream at full rate; more only lengthens the queues, and with
+// them every dependent load at a unit boundary. Head_dim 64 (a quarter of
+// the bytes per step) uses three.
 constexpr int decode_waves_per_simd(int head_dim, bool kv8) {
-  return (void)kv8, head_dim >= 256 ? 1 : head_dim == 128 ? 2 : 3;
+  return (void)kv8, head_dim >= 128 ? 1 : 3;
 }
 
 // One split request: its workspace slots are partial_base ..

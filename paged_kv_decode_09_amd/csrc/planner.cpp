@@ -181,8 +181,10 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
     split = p.fixed_split_size;
     unit_cap = std::min<int64_t>((int64_t)split * P, kMaxUnitTokens);
   } else if (B > 0) {
+    // units of about a kUnitsPerWorkgroup-th of a workgroup's share, so
+    // that no single long request decides when the last workgroup ends
     const int64_t units_wanted = slots * kUnitsPerWorkgroup;
-    if ((int64_t)B * p.num_kv_heads < units_wanted) {
+    {
       const int64_t total = attended * p.num_kv_heads;
       int64_t unit = std::max<int64_t>(kMinUnitTokens, (total + units_wanted - 1) / units_wanted);
       // an even number of steps for every wavefront of the workgroup
