@@ -207,20 +207,18 @@ __device__ __forceinline__ float load_coherent1(__amdgpu_buffer_rsrc_t r, uint32
 
 // merge_states for one (request, kv head) of a split request: fold the G
 // heads' states of `count` workspace slots first, first + stride, ...
-// (normalised outputs, base-2 LSE) by log-sum-exp, strictly in slot order.
-// The result goes to o and the natural-log lse (out_slot < 0), or, as a
-// state of the same form, to workspace slot out_slot (one of the inputs:
-// each thread reads its column of every input before it writes it, and the
-// LSEs are read into LDS before any is written).
+// (normalised outputs, base-2 LSE) by log-sum-exp, in slot order. The
+// result goes to o and the natural-log lse (out_slot < 0), or, as a state
+// of the same form, to workspace slot out_slot (then one of the inputs, and
+// count <= kBatch: every thread has its inputs before any thread writes).
 //
-// The LSEs are staged in LDS (`stage`, `stage_floats` floats; if they do not
-// fit, each thread reads them itself, which is only done when the result
-// goes to o). Each thread owns one float4 column of one head and loads the
-// inputs eight at a time, so that eight loads are in flight.
+// Each thread owns one float4 column of one head and loads the outputs and
+// LSEs of kBatch slots at once; a later batch rescales the running sums to
+// the new maximum.
 template <int HD>
 __device__ void merge_partials(const DecodeArgs& a, int request, int qh0, int first, int stride,
-                               int count, int out_slot, float* stage, int stage_floats) {
-  constexpr int kBatch = 8;
+                               int count, int out_slot) {
+  constexpr int kBatch = HD >= 128 ? 16 : 8;
   constexpr int cols4 = HD / 4;
   const int n = count;
   const int G = a.group;
@@ -230,43 +228,47 @@ __device__ void merge_partials(const DecodeArgs& a, int request, int qh0, int fi
       make_rsrc(a.ws_o + (size_t)first * nq * HD, (uint32_t)(span * nq * HD * 4));
   const __amdgpu_buffer_rsrc_t rl =
       make_rsrc(a.ws_lse + (size_t)first * nq, (uint32_t)(span * nq * 4));
-  const bool staged = n * G <= stage_floats;
-  if (staged) {
-    for (int e = threadIdx.x; e < n * G; e += kWaves * 64) {
-      const int k = e / G, h = e - k * G;
-      stage[e] = load_coherent1(rl, (uint32_t)(k * stride * nq + qh0 + h) * 4);
-    }
-  }
-  lds_barrier();
-  for (int e = threadIdx.x; e < G * cols4; e += kWaves * 64) {
-    const int h = e / cols4, c4 = e - h * cols4;
-    auto lse_of = [&](int k) {
-      return staged ? stage[k * G + h]
-                    : load_coherent1(rl, (uint32_t)(k * stride * nq + qh0 + h) * 4);
-    };
-    float M = -INFINITY;
-    for (int k = 0; k < n; ++k) M = fmaxf(M, lse_of(k));
-    float den = 0.0f;
+  for (int e0 = 0; e0 < G * cols4; e0 += kWaves * 64) {
+    const int e = e0 + (int)threadIdx.x;
+    const bool active = e < G * cols4;
+    const int h = active ? e / cols4 : 0, c4 = active ? e - h * cols4 : 0;
+    float M = -INFINITY, den = 0.0f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-      for (int k0 = 0; k0 < n; k0 += kBatch) {
-        f32x4 x[kBatch];
+    for (int k0 = 0; k0 < n; k0 += kBatch) {
+      f32x4 x[kBatch];
+      float l[kBatch];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int k = min(k0 + j, n - 1);
-          x[j] = load_coherent4(ro, (uint32_t)((k * stride * nq + qh0 + h) * HD + 4 * c4) * 4);
-        }
+      for (int j = 0; j < kBatch; ++j) {
+        const int k = min(k0 + j, n - 1) * stride;
+        x[j] = load_coherent4(ro, (uint32_t)((k * nq + qh0 + h) * HD + 4 * c4) * 4);
+        l[j] = load_coherent1(rl, (uint32_t)(k * nq + qh0 + h) * 4);
+      }
+      float bm = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (k0 + j < n) bm = fmaxf(bm, l[j]);
+      const float Mn = fmaxf(M, bm);
+      if (Mn != -INFINITY) {
+        const float sc = M == -INFINITY ? 0.0f : fast_exp2(M - Mn);
+        den *= sc;
+        num *= sc;
 #pragma unroll
         for (int j = 0; j < kBatch; ++j) {
           if (k0 + j < n) {
-            const float lk = lse_of(k0 + j);
-            const float wk = lk == -INFINITY ? 0.0f : fast_exp2(lk - M);
+            const float wk = l[j] == -INFINITY ? 0.0f : fast_exp2(l[j] - Mn);
             den += wk;
             num += wk * x[j];
           }
         }
+        M = Mn;
       }
     }
+    if (out_slot >= 0) {
+      // in place: every thread holds its inputs before any thread writes
+      wait_vector_memory();
+      lds_barrier();
+    }
+    if (!active) continue;
     const float lse2 = den > 0.0f ? M + __builtin_amdgcn_logf(den) : -INFINITY;
     if (out_slot < 0) {
       const size_t orow = (size_t)request * nq + qh0 + h;
@@ -671,14 +673,11 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
       const int slot0 = cu.partial - cu.chunk;
       int32_t* cnt = a.merge_counters +
                      ((size_t)cu.request * a.num_kv_heads + cu.kv_head) * a.merge_stride;
-      float* stage = reinterpret_cast<float*>(smem);
-      const int stage_floats = kWaves * G_::kWaveLds / 4;
       if (threadIdx.x == 0) s_last = atomicAdd(cnt + 1 + run, 1) == run_len - 1;
       lds_barrier();
       if (__builtin_amdgcn_readfirstlane(s_last)) {
         const int rslot = slot0 + run * kMergeGroup;
-        merge_partials<HD>(a, cu.request, qh0, rslot, 1, run_len, runs == 1 ? -1 : rslot,
-                           stage, stage_floats);
+        merge_partials<HD>(a, cu.request, qh0, rslot, 1, run_len, runs == 1 ? -1 : rslot);
         if (threadIdx.x == 0) atomicExch(cnt + 1 + run, 0);   // ready for the next launch
         if (runs > 1) {
           wait_vector_memory();
@@ -686,8 +685,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
           if (threadIdx.x == 0) s_last = atomicAdd(cnt, 1) == runs - 1;
           lds_barrier();
           if (__builtin_amdgcn_readfirstlane(s_last)) {
-            merge_partials<HD>(a, cu.request, qh0, slot0, kMergeGroup, runs, -1, stage,
-                               stage_floats);
+            merge_partials<HD>(a, cu.request, qh0, slot0, kMergeGroup, runs, -1);
             if (threadIdx.x == 0) atomicExch(cnt, 0);
           }
         }

@@ -269,6 +269,10 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
   out->items.resize(units.size());
   for (size_t k = 0; k < units.size(); ++k) out->items[k] = units[k].it;
 
+  // the merge counters are addressed with 32-bit byte offsets
+  if ((int64_t)B * p.num_kv_heads * (1 + (out->max_units + kMergeGroup - 1) / kMergeGroup) * 4 >
+      INT32_MAX / 2)
+    return fail(PKD_EUNSUPPORTED, "too many split requests for the merge counters");
   // the merge addresses one request's partial states with 32-bit offsets
   if ((int64_t)partials * p.num_qo_heads * p.head_dim * 4 > INT32_MAX)
     return fail(PKD_EUNSUPPORTED, fmt("%d partial states of %d heads x %d exceed the "
