@@ -173,6 +173,8 @@ void pkd_plan_destroy(pkd_plan* plan);
  * Runs of one plan must not overlap in time (for example on two streams):
  * the workgroups share work and merge counters owned by the plan. Runs of
  * different plans may overlap.
+ * Alignment: q, k_cache, v_cache 16 bytes (and page_stride a multiple of 16
+ * bytes), o 8 bytes, workspace 256 bytes.
  * Errors: PKD_EINVAL (null pointer, page_stride too small, misaligned
  * buffer), PKD_EWORKSPACE, PKD_EHIP (launch failure). */
 pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,

@@ -84,6 +84,8 @@ pkd_status check_run(const pkd_plan* plan, const void* q, const void* k,
     return pkd::fail(PKD_EINVAL,
                      "q, k_cache and v_cache must be 16-byte aligned and the page "
                      "stride a multiple of 16 bytes");
+  if (reinterpret_cast<uintptr_t>(o) % 8 != 0)
+    return pkd::fail(PKD_EINVAL, "o must be 8-byte aligned");
   const size_t need = plan->host.info.workspace_bytes;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need))
     return pkd::fail(PKD_EWORKSPACE, "workspace of " + std::to_string(workspace_bytes) +
@@ -219,6 +221,7 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
   a.lse = lse;
   const int32_t parts = plan->host.info.num_partials;
   a.ws_o = reinterpret_cast<float*>(workspace);
+  a.ws_o_bytes = (size_t)parts * p.num_qo_heads * p.head_dim * 4;
   a.ws_lse = parts > 0 ? reinterpret_cast<float*>(
                              reinterpret_cast<char*>(workspace) +
                              pkd::workspace_lse_offset(parts, p.num_qo_heads, p.head_dim))

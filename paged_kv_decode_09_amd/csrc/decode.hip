@@ -142,6 +142,19 @@ __device__ __forceinline__ void wait_vector_memory() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
+// Four consecutive outputs (idx a multiple of 4) in one 8-byte store.
+__device__ __forceinline__ void store_out4(void* base, size_t idx, f32x4 v, int bf16) {
+  u32x2 w;
+  if (bf16) {
+    w[0] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){v[0], v[1]}, bf16x2));
+    w[1] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){v[2], v[3]}, bf16x2));
+  } else {
+    w[0] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){v[0], v[1]}, f16x2));
+    w[1] = __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){v[2], v[3]}, f16x2));
+  }
+  *reinterpret_cast<u32x2*>(reinterpret_cast<char*>(base) + idx * 2) = w;
+}
+
 __device__ __forceinline__ void store_out(void* base, size_t idx, float v, int bf16) {
   if (bf16)
     reinterpret_cast<__bf16*>(base)[idx] = (__bf16)v;
@@ -203,6 +216,10 @@ __device__ __forceinline__ f32x4 load_coherent4(__amdgpu_buffer_rsrc_t r, uint32
 }
 __device__ __forceinline__ float load_coherent1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCoherentPolicy));
+}
+// 16-byte store with the same policy as store_coherent.
+__device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherentPolicy);
 }
 
 // merge_states for one (request, kv head) of a split request: fold the G
@@ -487,6 +504,10 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
     }
   };
 
+  // the partial outputs, for 16-byte device-coherent stores
+  const __amdgpu_buffer_rsrc_t ws_o_rsrc =
+      make_rsrc(a.ws_o, (uint32_t)min<size_t>(a.ws_o_bytes, 0xFFFFFFF0u));
+
   // ---- Units form a pipeline per workgroup. While unit `cur` is attended,
   // the item and the page ids of the next unit `nxt` are loaded, and the
   // last load issue of cur's step loop is nxt's first step, so that cur's
@@ -630,30 +651,34 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
     lds_barrier();
     // the unit after nxt: its item, to be read during nxt
     const int nxt2 = __builtin_amdgcn_readfirstlane(s_ticket[par]);
-    // ---- merge the wavefronts' states, in wavefront order
-    const int total = group * HD;
-    for (int e = threadIdx.x; e < total; e += kWaves * 64) {
-      const int h = e / HD, c = e - h * HD;
+    // ---- merge the wavefronts' states, in wavefront order: one float4
+    // column of one head per thread
+    constexpr int cols4 = HD / 4;
+    for (int e = threadIdx.x; e < group * cols4; e += kWaves * 64) {
+      const int h = e / cols4, c = 4 * (e - h * cols4);
       float M = s_m[0][h];
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-      float num = 0.0f, den = 0.0f;
+      f32x4 num = {0.f, 0.f, 0.f, 0.f};
+      float den = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
         const float mw = s_m[w][h];
         const float sw = mw == -INFINITY ? 0.0f : fast_exp2(mw - M);
-        num += sw * reinterpret_cast<const float*>(smem + w * G_::kWaveLds)[h * HD + c];
+        num += sw * *reinterpret_cast<const f32x4*>(smem + w * G_::kWaveLds + (h * HD + c) * 4);
         den += sw * s_d[w][h];
       }
-      const float ov = num / den * a.v_scale;
+      f32x4 ov;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = num[i] / den * a.v_scale;
       const float lse2 = M + __builtin_amdgcn_logf(den);
       const int qh = qh0 + h;
       if (cu.partial < 0) {
-        store_out(a.o, ((size_t)cu.request * a.num_qo_heads + qh) * HD + c, ov, a.o_bf16);
+        store_out4(a.o, ((size_t)cu.request * a.num_qo_heads + qh) * HD + c, ov, a.o_bf16);
         if (a.lse != nullptr && c == 0) a.lse[(size_t)cu.request * a.num_qo_heads + qh] = lse2 * kLn2;
       } else {
         // device-coherent stores: the merging workgroup may sit on another XCD
-        store_coherent(a.ws_o + ((size_t)cu.partial * a.num_qo_heads + qh) * HD + c, ov);
+        store_coherent4(ws_o_rsrc, (uint32_t)(((size_t)cu.partial * a.num_qo_heads + qh) * HD + c) * 4, ov);
         if (c == 0) store_coherent(a.ws_lse + (size_t)cu.partial * a.num_qo_heads + qh, lse2);
       }
     }

@@ -95,6 +95,7 @@ struct DecodeArgs {
   void* o;
   float* lse;
   float* ws_o;          // [num_partials][num_qo_heads][head_dim]
+  size_t ws_o_bytes;
   float* ws_lse;        // [num_partials][num_qo_heads], base-2
   int64_t page_stride;  // elements between pages
   int32_t slot_stride;  // elements between tokens of a page
