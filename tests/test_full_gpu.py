@@ -202,3 +202,24 @@ def test_host_planning_matches_the_device_occupancy(hd, kv):
     assert plan.info.workgroups_per_cu == info.workgroups_per_cu
     assert plan.info.num_workgroups == info.num_workgroups
     assert plan.info.num_items == info.num_items
+
+
+def test_many_runs_merge_matches_the_oracle_and_repeats():
+    """A 60000-token request under a one-page fixed split has 3750 units
+    per kv head: 469 runs of 8, whose final fold takes 30 batches (the
+    running-maximum rescale between batches). Checked against the oracle,
+    and bitwise against a second run of the same plan (the merge counters
+    must be back to zero after a launch)."""
+    from dataclasses import replace
+    w = replace(wl.WORKLOADS["long_context"], name="many_runs", seed=11, batch=2,
+                lengths=("fixed", [60000, 3001]), fixed_split_size=1)
+    case = wl.make_case(w, device="cuda")
+    o, lse, plan = run_gpu(w, case)
+    say("many_runs units", plan.info.num_items, "partials", plan.info.num_partials)
+    assert plan.info.num_items == (3750 + 188) * w.num_kv_heads
+    ref_o, ref_l = oracle_for(w, case)
+    eo, el = max_abs(o, ref_o), max_abs(lse, ref_l)
+    say("many_runs o max-abs", eo, "lse max-abs", el)
+    assert eo <= o_tol(w) and el <= LSE_TOL
+    o2, lse2, _ = run_gpu(w, case, plan=plan)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
