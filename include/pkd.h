@@ -170,9 +170,11 @@ void pkd_plan_destroy(pkd_plan* plan);
  * head) merges that request's partials for the head by log-sum-exp in
  * ascending chunk order (merge_states named with fixed_split_size), so the
  * result does not depend on which workgroup ran which unit.
+ * Workgroups that run out of units may take a long unit another workgroup
+ * holds in reserve; which workgroup runs a unit never changes the result.
  * Runs of one plan must not overlap in time (for example on two streams):
- * the workgroups share work and merge counters owned by the plan. Runs of
- * different plans may overlap.
+ * the workgroups share work counters, reserve slots and merge counters
+ * owned by the plan. Runs of different plans may overlap.
  * Alignment: q, k_cache, v_cache 16 bytes (and page_stride a multiple of 16
  * bytes), o 8 bytes, workspace 256 bytes.
  * Errors: PKD_EINVAL (null pointer, page_stride too small, misaligned

@@ -19,8 +19,9 @@ struct pkd_plan {
   void* staging = nullptr;            // pinned host copy used by the upload
   hipEvent_t uploaded = nullptr;
   int device = 0;
-  // Device copy, all uploaded from the staging copy (counters as zeros):
-  // the work counters, the per-(request, kv head) merge counters, the items.
+  // Device copy, all uploaded from the staging copy: the work counters
+  // (zeros), the reserve slots (0xFFFFFFFF: never published), the
+  // per-(request, kv head) merge counters (zeros), the items.
   static constexpr size_t kCounterBytes = 64;
   int32_t merge_stride() const {
     return 1 + (host.max_units + pkd::kMergeGroup - 1) / pkd::kMergeGroup;
@@ -30,13 +31,21 @@ struct pkd_plan {
         (size_t)host.params.batch_size * host.params.num_kv_heads * merge_stride() * 4;
     return (n + 63) & ~(size_t)63;
   }
+  size_t reserve_bytes() const {
+    return ((size_t)host.info.num_workgroups * 2 * 4 + 63) & ~(size_t)63;   // two per workgroup
+  }
   int32_t* d_counters() const { return reinterpret_cast<int32_t*>(dev); }
-  int32_t* d_merge_counters() const {
+  int32_t* d_reserve() const {
     return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(dev) + kCounterBytes);
+  }
+  int32_t* d_merge_counters() const {
+    return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(dev) + kCounterBytes +
+                                      reserve_bytes());
   }
   const pkd_work_item* d_items() const {
     return reinterpret_cast<const pkd_work_item*>(reinterpret_cast<const char*>(dev) +
-                                                  kCounterBytes + merge_counter_bytes());
+                                                  kCounterBytes + reserve_bytes() +
+                                                  merge_counter_bytes());
   }
 };
 
@@ -59,7 +68,7 @@ void free_plan(pkd_plan* p) {
 
 size_t plan_bytes(const pkd_plan& p) {
   if (p.host.items.empty()) return 0;
-  return pkd_plan::kCounterBytes + p.merge_counter_bytes() +
+  return pkd_plan::kCounterBytes + p.reserve_bytes() + p.merge_counter_bytes() +
          p.host.items.size() * sizeof(pkd_work_item);
 }
 
@@ -168,9 +177,11 @@ pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
                                        hipGetErrorString(e));
     }
     char* s = reinterpret_cast<char*>(p->staging);
-    const size_t zeros = pkd_plan::kCounterBytes + p->merge_counter_bytes();
-    std::memset(s, 0, zeros);
-    std::memcpy(s + zeros, p->host.items.data(),
+    std::memset(s, 0, pkd_plan::kCounterBytes);
+    std::memset(s + pkd_plan::kCounterBytes, 0xFF, p->reserve_bytes());
+    const size_t zeros = pkd_plan::kCounterBytes + p->reserve_bytes();
+    std::memset(s + zeros, 0, p->merge_counter_bytes());
+    std::memcpy(s + zeros + p->merge_counter_bytes(), p->host.items.data(),
                 p->host.items.size() * sizeof(pkd_work_item));
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     e = hipMemcpyAsync(p->dev, p->staging, bytes, hipMemcpyHostToDevice, hs);
@@ -209,6 +220,7 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
     return pkd::fail(PKD_EINVAL, "q_scale, k_scale and v_scale must be finite");
   pkd::DecodeArgs a{};
   a.counters = plan->d_counters();
+  a.reserve = plan->d_reserve();
   a.merge_counters = plan->d_merge_counters();
   a.merge_stride = plan->merge_stride();
   a.num_items = plan->host.info.num_items;
@@ -247,6 +259,7 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
   a.cap = cap ? p.logits_soft_cap : 0.0f;
   a.inv_cap = cap ? 1.0f / p.logits_soft_cap : 0.0f;
   a.v_scale = v_scale;
+  a.steal_limit = plan->host.steal_limit;
   int e = pkd::launch_decode(p, a, plan->host.info.num_workgroups, stream);
   if (e != hipSuccess) return hip_fail((hipError_t)e, "decode launch");
   return PKD_OK;

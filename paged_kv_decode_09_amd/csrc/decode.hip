@@ -344,6 +344,8 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   __shared__ float s_d[kWaves][kMaxGroup];
   __shared__ int s_ticket[2];
   __shared__ int s_last;
+  __shared__ unsigned long long s_steal;
+  __shared__ int s_drop;
 
   const int lane = threadIdx.x & 63;
   // wave-uniform (an SGPR), so that the step loop branches on scalars
@@ -508,6 +510,10 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   const __amdgpu_buffer_rsrc_t ws_o_rsrc =
       make_rsrc(a.ws_o, (uint32_t)min<size_t>(a.ws_o_bytes, 0xFFFFFFF0u));
 
+  // reserve slots of all workgroups, two each (by unit parity)
+  const int nslots = 2 * (int)gridDim.x;
+  const __amdgpu_buffer_rsrc_t res_rsrc = make_rsrc(a.reserve, (uint32_t)nslots * 4);
+
   // ---- Units form a pipeline per workgroup. While unit `cur` is attended,
   // the item and the page ids of the next unit `nxt` are loaded, and the
   // last load issue of cur's step loop is nxt's first step, so that cur's
@@ -517,213 +523,319 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   // Its first two units are items blockIdx.x and blockIdx.x + gridDim.x
   // (the grid never exceeds the item count); later ones are tickets from
   // the plan's counter, offset by twice the grid size.
+  //
+  // A long enough held unit nxt (an item below a.steal_limit) is published
+  // in a reserve slot from the time its ticket is known until cur's last
+  // issue, when thread 0 claims it. A workgroup whose own chain has run out
+  // takes published units of others (a "steal"); an owner that finds its
+  // claimed unit stolen (told at the unit's first step) masks the rest of
+  // it (no arithmetic, no outputs), which keeps its pipeline going. Every
+  // unit is processed by exactly one workgroup. Thread 0 alone publishes
+  // and claims, so its claim is ordered after its publication, and its
+  // publication after its previous claim of the slot (whose result it has
+  // read).
   int cur = blockIdx.x;
-  Unit cu = unit_from_lanes(load_item_lanes(a.items, cur, lane));
   int nxt = cur + (int)gridDim.x;
-  {
-    const Win W = first_window(cu, s_pages[0]);
-    const int wpages = (W.whi >> lp) - W.wpage0 + 1;
-    const int32_t* pidx = a.indices + cu.page_base;
-    for (int i = threadIdx.x; i < wpages; i += kWaves * 64) s_pages[0][i] = pidx[W.wpage0 + i];
-  }
-  lds_barrier();
+  if (threadIdx.x == 0 && nxt < a.steal_limit)
+    __hip_atomic_store(a.reserve + 2 * blockIdx.x + 1, nxt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   StepRegs<G_::kPieces> A, B;
-  issue(first_window(cu, s_pages[0]), wave, A);
-  load_q(cu);
-  unsigned itemv = load_item_lanes(a.items, min(nxt, last_item), lane);   // item of nxt
+  Unit cu;
+  unsigned itemv;
+  unsigned claim = 0;     // what thread 0's claim of cur returned
+  bool claimed = false;   // cur was published and claimed by this workgroup
   int buf = 0, par = 0;
 
-  while (cur < a.num_items) {
-    // ---- unit start: cur's first step is in flight in A, its q in bq, the
-    // item of nxt in itemv
-    int tk = 0;
-    if (threadIdx.x == 0) tk = atomicAdd(&a.counters[0], 1);   // the unit after nxt
-    // nxt (read after cur's first step): its first page window (the first
-    // kWaves*64 pages now, to LDS at cur's end; more, rarely, then), and the
-    // pages of this wave's first step of nxt (for the hand-over issue)
-    Unit nu;
-    Win Wn;
-    int nwpages, pgn, hpg0, hpg1;
-    const int32_t* npidx;
-    auto load_next = [&]() {
-      nu = unit_from_lanes(itemv);
-      Wn = first_window(nu, s_pages[buf ^ 1]);
-      nwpages = (Wn.whi >> lp) - Wn.wpage0 + 1;
-      npidx = a.indices + nu.page_base;
-      pgn = npidx[Wn.wpage0 + min((int)threadIdx.x, nwpages - 1)];
-      hpg0 = npidx[token(Wn, wave, tau0) >> lp];
-      hpg1 = npidx[token(Wn, wave, tau1) >> lp];
-    };
-
-    m_run = -INFINITY;
-    d_run = 0.0f;
+  // A published unit of another workgroup, or -1 when none is left. Slots
+  // are scanned from this workgroup's right neighbour on, so that thieves
+  // spread over the owners; a lost compare-and-swap scans again.
+  auto steal = [&]() {
+    // an opaque copy of the thread index, so that the scan's addresses are
+    // computed here and not kept in registers through the decode loop
+    int tid = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    for (int tries = 0; tries < 4; ++tries) {
+      // (scan position << 32 | unit) of the first published slot, by an LDS
+      // minimum over the workgroup
+      if (tid == 0) s_steal = ~0ull;
+      lds_barrier();
+      unsigned long long best = ~0ull;
+      for (int i0 = 0; i0 < nslots; i0 += 8 * kWaves * 64) {
+        // all eight loads in flight at once (positions past the end load
+        // the last slot again and are ignored)
+        unsigned v[8];
 #pragma unroll
-    for (int b = 0; b < G_::kPvMfma; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    const int base = cu.tb & ~(kStepTokens - 1);
-    const int nsteps = (cu.te - base + kStepTokens - 1) / kStepTokens;
-    const int qh0 = cu.kv_head * group;
-
-    // Steps are processed in windows whose pages fit the LDS page table. A
-    // wave takes every kWaves-th step of a window, one step ahead of the
-    // loads (buffers A and B alternate); the count is padded to an even
-    // number >= 4 with steps past the window, which read clamped rows and
-    // whose tokens are all masked (no effect on the state). The first and
-    // the last half-step are peeled and the loop body runs at least once,
-    // so that the same loads are in flight on every path through it and the
-    // compiler's wait before a step covers that step's loads only. The last
-    // issue of the last window is the next unit's first step.
-    int w0 = 0;
-    do {
-      const int w1 = min(nsteps, w0 + win_steps);
-      Win W;
-      W.base = base;
-      W.wlo = max(cu.tb, base + w0 * kStepTokens);
-      W.whi = min(cu.te, base + w1 * kStepTokens) - 1;
-      W.wpage0 = W.wlo >> lp;
-      W.sp = s_pages[buf];
-      W.head_off = (int64_t)cu.kv_head * a.head_stride;
-      const int s0 = w0 + ((wave - w0) % kWaves + kWaves) % kWaves;
-      const int mine = s0 < w1 ? (w1 - s0 + kWaves - 1) / kWaves : 0;
-      const int m2 = max(4, (mine + 1) & ~1);
-      if (w0 > 0) {
-        // a later window: its pages replace the previous window's
-        lds_barrier();
-        const int wpages = (W.whi >> lp) - W.wpage0 + 1;
-        const int32_t* pidx = a.indices + cu.page_base;
-        for (int i = threadIdx.x; i < wpages; i += kWaves * 64) s_pages[buf][i] = pidx[W.wpage0 + i];
-        lds_barrier();
-        issue(W, s0, A);
-      }
-      // The scheduling barriers keep each issue ahead of the step it overlaps:
-      // the loads must leave before the wait for the previous step's rows.
-      issue(W, s0 + kWaves, B);
-      __builtin_amdgcn_sched_barrier(0);
-      consume(W, s0, A);
-      __builtin_amdgcn_sched_barrier(0);
-      load_next();                       // again (same loads) in a later window
-      __builtin_amdgcn_sched_barrier(0);
-      int j = 1;
-      do {
-        issue(W, s0 + (j + 1) * kWaves, A);
-        __builtin_amdgcn_sched_barrier(0);
-        consume(W, s0 + j * kWaves, B);
-        __builtin_amdgcn_sched_barrier(0);
-        issue(W, s0 + (j + 2) * kWaves, B);
-        __builtin_amdgcn_sched_barrier(0);
-        consume(W, s0 + (j + 1) * kWaves, A);
-        __builtin_amdgcn_sched_barrier(0);
-        j += 2;
-      } while (j + 1 < m2);
-      {
-        // last issue: the next unit's first step after the last window,
-        // else a clamped surplus step of this window
-        const bool hand = w1 == nsteps;
-        const int c0 = token(W, s0 + m2 * kWaves, tau0);
-        const int c1 = token(W, s0 + m2 * kWaves, tau1);
-        const int pg0 = W.sp[(c0 >> lp) - W.wpage0];
-        const int pg1 = W.sp[(c1 >> lp) - W.wpage0];
-        issue_rows(hand ? Wn : W, hand ? token(Wn, wave, tau0) : c0,
-                   hand ? token(Wn, wave, tau1) : c1, hand ? hpg0 : pg0, hand ? hpg1 : pg1, A);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      consume(W, s0 + (m2 - 1) * kWaves, B);
-      __builtin_amdgcn_sched_barrier(0);
-      w0 = w1;
-    } while (w0 < nsteps);
-
-    // ---- end of cur: nxt's pages and the ticket, this wave's state to LDS
-    if ((int)threadIdx.x < nwpages) s_pages[buf ^ 1][threadIdx.x] = pgn;
-    for (int i = threadIdx.x + kWaves * 64; i < nwpages; i += kWaves * 64)
-      s_pages[buf ^ 1][i] = npidx[Wn.wpage0 + i];
-    if (threadIdx.x == 0) s_ticket[par] = 2 * (int)gridDim.x + tk;
-    d_run = wave_sum_over_groups(d_run);
-    float* sacc = reinterpret_cast<float*>(vl);   // [16 heads][HD], own region
-    if (n < group) {
+        for (int k = 0; k < 8; ++k) {
+          const int i = min(i0 + k * kWaves * 64 + tid, nslots - 1);
+          int slot = 2 * (int)blockIdx.x + 2 + i;
+          slot = slot >= nslots ? slot - nslots : slot;
+          v[k] = __builtin_amdgcn_raw_buffer_load_b32(res_rsrc, (uint32_t)slot * 4u, 0, kCoherentPolicy);
+        }
 #pragma unroll
-      for (int b = 0; b < G_::kPvMfma; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[n * HD + 16 * b + 4 * g + i] = acc[b][i];
-      if (g == 0) {
-        s_m[wave][n] = m_run;
-        s_d[wave][n] = d_run;
+        for (int k = 0; k < 8; ++k) {
+          const int i = i0 + k * kWaves * 64 + tid;
+          const unsigned long long key = ((unsigned long long)i << 32) | v[k];
+          best = i < nslots && v[k] < kMaxItems && key < best ? key : best;
+        }
       }
+      if (best != ~0ull) atomicMin(&s_steal, best);
+      lds_barrier();
+      best = s_steal;
+      lds_barrier();
+      const int i = __builtin_amdgcn_readfirstlane((int)(best >> 32));
+      const int v = __builtin_amdgcn_readfirstlane((int)(unsigned)best);
+      if (i < 0) return -1;                 // nothing published
+      int slot = 2 * (int)blockIdx.x + 2 + i;
+      slot = slot >= nslots ? slot - nslots : slot;
+      if (tid == 0) s_steal = atomicCAS(a.reserve + slot, v, (int)kStolen) == v;
+      lds_barrier();
+      const bool won = __builtin_amdgcn_readfirstlane((int)s_steal) != 0;
+      lds_barrier();
+      if (won) return v;
+    }
+    return -1;
+  };
+
+  for (;;) {
+    // ---- chain start: cur's item, first page window and first step, its q,
+    // and the item of nxt
+    cu = unit_from_lanes(load_item_lanes(a.items, cur, lane));
+    {
+      const Win W = first_window(cu, s_pages[buf]);
+      const int wpages = (W.whi >> lp) - W.wpage0 + 1;
+      const int32_t* pidx = a.indices + cu.page_base;
+      for (int i = threadIdx.x; i < wpages; i += kWaves * 64) s_pages[buf][i] = pidx[W.wpage0 + i];
     }
     lds_barrier();
-    // the unit after nxt: its item, to be read during nxt
-    const int nxt2 = __builtin_amdgcn_readfirstlane(s_ticket[par]);
-    // ---- merge the wavefronts' states, in wavefront order: one float4
-    // column of one head per thread
-    constexpr int cols4 = HD / 4;
-    for (int e = threadIdx.x; e < group * cols4; e += kWaves * 64) {
-      const int h = e / cols4, c = 4 * (e - h * cols4);
-      float M = s_m[0][h];
+    issue(first_window(cu, s_pages[buf]), wave, A);
+    load_q(cu);
+    itemv = load_item_lanes(a.items, min(nxt, last_item), lane);   // item of nxt
+
+    while (cur < a.num_items) {
+      // ---- unit start: cur's first step is in flight in A, its q in bq, the
+      // item of nxt in itemv
+      // the unit after nxt (none once the tickets are spent)
+      int tk = a.num_items;
+      if (threadIdx.x == 0 && nxt < a.num_items) tk = atomicAdd(&a.counters[0], 1);
+      // nxt (read after cur's first step): its first page window (the first
+      // kWaves*64 pages now, to LDS at cur's end; more, rarely, then), and the
+      // pages of this wave's first step of nxt (for the hand-over issue)
+      Unit nu;
+      Win Wn;
+      int nwpages, pgn, hpg0, hpg1;
+      const int32_t* npidx;
+      auto load_next = [&]() {
+        nu = unit_from_lanes(itemv);
+        Wn = first_window(nu, s_pages[buf ^ 1]);
+        nwpages = (Wn.whi >> lp) - Wn.wpage0 + 1;
+        npidx = a.indices + nu.page_base;
+        pgn = npidx[Wn.wpage0 + min((int)threadIdx.x, nwpages - 1)];
+        hpg0 = npidx[token(Wn, wave, tau0) >> lp];
+        hpg1 = npidx[token(Wn, wave, tau1) >> lp];
+      };
+
+      m_run = -INFINITY;
+      d_run = 0.0f;
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
-      f32x4 num = {0.f, 0.f, 0.f, 0.f};
-      float den = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = s_m[w][h];
-        const float sw = mw == -INFINITY ? 0.0f : fast_exp2(mw - M);
-        num += sw * *reinterpret_cast<const f32x4*>(smem + w * G_::kWaveLds + (h * HD + c) * 4);
-        den += sw * s_d[w][h];
-      }
-      f32x4 ov;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ov[i] = num[i] / den * a.v_scale;
-      const float lse2 = M + __builtin_amdgcn_logf(den);
-      const int qh = qh0 + h;
-      if (cu.partial < 0) {
-        store_out4(a.o, ((size_t)cu.request * a.num_qo_heads + qh) * HD + c, ov, a.o_bf16);
-        if (a.lse != nullptr && c == 0) a.lse[(size_t)cu.request * a.num_qo_heads + qh] = lse2 * kLn2;
-      } else {
-        // device-coherent stores: the merging workgroup may sit on another XCD
-        store_coherent4(ws_o_rsrc, (uint32_t)(((size_t)cu.partial * a.num_qo_heads + qh) * HD + c) * 4, ov);
-        if (c == 0) store_coherent(a.ws_lse + (size_t)cu.partial * a.num_qo_heads + qh, lse2);
-      }
-    }
-    if (cu.partial >= 0) {
-      // Count this unit once its partial state has reached the device-coherent
-      // level. Units are merged in runs of kMergeGroup consecutive units, then
-      // the runs: the workgroup that counts the last unit of a run merges the
-      // run into the run's first slot (or straight into o if the request has
-      // a single run), and the one that counts the last run merges the runs.
-      // Which workgroups these are does not change the result.
-      wait_vector_memory();
-      lds_barrier();
-      const int n = cu.num_chunks;
-      const int run = cu.chunk / kMergeGroup;
-      const int runs = (n + kMergeGroup - 1) / kMergeGroup;
-      const int run_len = min(kMergeGroup, n - run * kMergeGroup);
-      const int slot0 = cu.partial - cu.chunk;
-      int32_t* cnt = a.merge_counters +
-                     ((size_t)cu.request * a.num_kv_heads + cu.kv_head) * a.merge_stride;
-      if (threadIdx.x == 0) s_last = atomicAdd(cnt + 1 + run, 1) == run_len - 1;
-      lds_barrier();
-      if (__builtin_amdgcn_readfirstlane(s_last)) {
-        const int rslot = slot0 + run * kMergeGroup;
-        merge_partials<HD>(a, cu.request, qh0, rslot, 1, run_len, runs == 1 ? -1 : rslot);
-        if (threadIdx.x == 0) atomicExch(cnt + 1 + run, 0);   // ready for the next launch
-        if (runs > 1) {
-          wait_vector_memory();
+      for (int b = 0; b < G_::kPvMfma; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      const int base = cu.tb & ~(kStepTokens - 1);
+      const int nsteps = (cu.te - base + kStepTokens - 1) / kStepTokens;
+      const int qh0 = cu.kv_head * group;
+
+      // Steps are processed in windows whose pages fit the LDS page table. A
+      // wave takes every kWaves-th step of a window, one step ahead of the
+      // loads (buffers A and B alternate); the count is padded to an even
+      // number >= 4 with steps past the window, which read clamped rows and
+      // whose tokens are all masked (no effect on the state). The first and
+      // the last half-step are peeled and the loop body runs at least once,
+      // so that the same loads are in flight on every path through it and the
+      // compiler's wait before a step covers that step's loads only. The last
+      // issue of the last window is the next unit's first step.
+      bool drop = false;      // cur was taken by another workgroup: no outputs
+      int w0 = 0;
+      do {
+        int w1 = min(nsteps, w0 + win_steps);
+        Win W;
+        W.base = base;
+        W.wlo = max(cu.tb, base + w0 * kStepTokens);
+        W.whi = min(cu.te, base + w1 * kStepTokens) - 1;
+        W.wpage0 = W.wlo >> lp;
+        W.sp = s_pages[buf];
+        W.head_off = (int64_t)cu.kv_head * a.head_stride;
+        const int s0 = w0 + ((wave - w0) % kWaves + kWaves) % kWaves;
+        const int mine = s0 < w1 ? (w1 - s0 + kWaves - 1) / kWaves : 0;
+        int m2 = max(4, (mine + 1) & ~1);
+        if (w0 > 0) {
+          // a later window: its pages replace the previous window's
           lds_barrier();
-          if (threadIdx.x == 0) s_last = atomicAdd(cnt, 1) == runs - 1;
+          const int wpages = (W.whi >> lp) - W.wpage0 + 1;
+          const int32_t* pidx = a.indices + cu.page_base;
+          for (int i = threadIdx.x; i < wpages; i += kWaves * 64) s_pages[buf][i] = pidx[W.wpage0 + i];
           lds_barrier();
-          if (__builtin_amdgcn_readfirstlane(s_last)) {
-            merge_partials<HD>(a, cu.request, qh0, slot0, kMergeGroup, runs, -1);
-            if (threadIdx.x == 0) atomicExch(cnt, 0);
+          issue(W, s0, A);
+        }
+        // The scheduling barriers keep each issue ahead of the step it overlaps:
+        // the loads must leave before the wait for the previous step's rows.
+        issue(W, s0 + kWaves, B);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(W, s0, A);
+        __builtin_amdgcn_sched_barrier(0);
+        load_next();                       // again (same loads) in a later window
+        if (w0 == 0 && claimed) {
+          // The claim of cur, made before its first step was issued, has
+          // returned with that step: tell the wavefronts whether cur was
+          // stolen. Then every later row is clamped to the first token (the
+          // only unmasked one), the step count is the minimum and the unit
+          // ends with this window.
+          if (threadIdx.x == 0) s_drop = (claim & kStolen) != 0;
+          lds_barrier();
+          drop = __builtin_amdgcn_readfirstlane(s_drop) != 0;
+          if (drop) {
+            W.whi = W.wlo;
+            m2 = 4;
+            w1 = nsteps;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        int j = 1;
+        do {
+          issue(W, s0 + (j + 1) * kWaves, A);
+          __builtin_amdgcn_sched_barrier(0);
+          consume(W, s0 + j * kWaves, B);
+          __builtin_amdgcn_sched_barrier(0);
+          issue(W, s0 + (j + 2) * kWaves, B);
+          __builtin_amdgcn_sched_barrier(0);
+          consume(W, s0 + (j + 1) * kWaves, A);
+          __builtin_amdgcn_sched_barrier(0);
+          j += 2;
+        } while (j + 1 < m2);
+        {
+          // last issue: the next unit's first step after the last window,
+          // else a clamped surplus step of this window
+          const bool hand = w1 == nsteps;
+          // Thread 0 claims nxt if it was published (after the last window);
+          // the other lanes, and earlier windows, fall outside the buffer and
+          // do nothing. The result is read with nxt's first step.
+          const uint32_t coff = hand && nxt < a.steal_limit && threadIdx.x == 0
+                                    ? (uint32_t)(2 * blockIdx.x + (par ^ 1)) * 4u
+                                    : 0x80000000u;
+          claim = (unsigned)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32((int)kClaimStep, res_rsrc,
+                                                                           coff, 0, 0);
+          const int c0 = token(W, s0 + m2 * kWaves, tau0);
+          const int c1 = token(W, s0 + m2 * kWaves, tau1);
+          const int pg0 = W.sp[(c0 >> lp) - W.wpage0];
+          const int pg1 = W.sp[(c1 >> lp) - W.wpage0];
+          issue_rows(hand ? Wn : W, hand ? token(Wn, wave, tau0) : c0,
+                     hand ? token(Wn, wave, tau1) : c1, hand ? hpg0 : pg0, hand ? hpg1 : pg1, A);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        consume(W, s0 + (m2 - 1) * kWaves, B);
+        __builtin_amdgcn_sched_barrier(0);
+        w0 = w1;
+      } while (w0 < nsteps);
+
+      // ---- end of cur: nxt's pages and the ticket, this wave's state to LDS
+      if ((int)threadIdx.x < nwpages) s_pages[buf ^ 1][threadIdx.x] = pgn;
+      for (int i = threadIdx.x + kWaves * 64; i < nwpages; i += kWaves * 64)
+        s_pages[buf ^ 1][i] = npidx[Wn.wpage0 + i];
+      if (threadIdx.x == 0) s_ticket[par] = 2 * (int)gridDim.x + tk;
+      d_run = wave_sum_over_groups(d_run);
+      float* sacc = reinterpret_cast<float*>(vl);   // [16 heads][HD], own region
+      if (n < group) {
+#pragma unroll
+        for (int b = 0; b < G_::kPvMfma; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[n * HD + 16 * b + 4 * g + i] = acc[b][i];
+        if (g == 0) {
+          s_m[wave][n] = m_run;
+          s_d[wave][n] = d_run;
+        }
+      }
+      lds_barrier();
+      // the unit after nxt: its item, to be read during nxt
+      const int nxt2 = __builtin_amdgcn_readfirstlane(s_ticket[par]);
+      if (threadIdx.x == 0 && nxt2 < a.steal_limit)
+        __hip_atomic_store(a.reserve + 2 * blockIdx.x + par, nxt2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // ---- merge the wavefronts' states, in wavefront order: one float4
+      // column of one head per thread
+      constexpr int cols4 = HD / 4;
+      for (int e = threadIdx.x; !drop && e < group * cols4; e += kWaves * 64) {
+        const int h = e / cols4, c = 4 * (e - h * cols4);
+        float M = s_m[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
+        f32x4 num = {0.f, 0.f, 0.f, 0.f};
+        float den = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float mw = s_m[w][h];
+          const float sw = mw == -INFINITY ? 0.0f : fast_exp2(mw - M);
+          num += sw * *reinterpret_cast<const f32x4*>(smem + w * G_::kWaveLds + (h * HD + c) * 4);
+          den += sw * s_d[w][h];
+        }
+        f32x4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = num[i] / den * a.v_scale;
+        const float lse2 = M + __builtin_amdgcn_logf(den);
+        const int qh = qh0 + h;
+        if (cu.partial < 0) {
+          store_out4(a.o, ((size_t)cu.request * a.num_qo_heads + qh) * HD + c, ov, a.o_bf16);
+          if (a.lse != nullptr && c == 0) a.lse[(size_t)cu.request * a.num_qo_heads + qh] = lse2 * kLn2;
+        } else {
+          // device-coherent stores: the merging workgroup may sit on another XCD
+          store_coherent4(ws_o_rsrc, (uint32_t)(((size_t)cu.partial * a.num_qo_heads + qh) * HD + c) * 4, ov);
+          if (c == 0) store_coherent(a.ws_lse + (size_t)cu.partial * a.num_qo_heads + qh, lse2);
+        }
+      }
+      if (!drop && cu.partial >= 0) {
+        // Count this unit once its partial state has reached the device-coherent
+        // level. Units are merged in runs of kMergeGroup consecutive units, then
+        // the runs: the workgroup that counts the last unit of a run merges the
+        // run into the run's first slot (or straight into o if the request has
+        // a single run), and the one that counts the last run merges the runs.
+        // Which workgroups these are does not change the result.
+        wait_vector_memory();
+        lds_barrier();
+        const int n = cu.num_chunks;
+        const int run = cu.chunk / kMergeGroup;
+        const int runs = (n + kMergeGroup - 1) / kMergeGroup;
+        const int run_len = min(kMergeGroup, n - run * kMergeGroup);
+        const int slot0 = cu.partial - cu.chunk;
+        int32_t* cnt = a.merge_counters +
+                       ((size_t)cu.request * a.num_kv_heads + cu.kv_head) * a.merge_stride;
+        if (threadIdx.x == 0) s_last = atomicAdd(cnt + 1 + run, 1) == run_len - 1;
+        lds_barrier();
+        if (__builtin_amdgcn_readfirstlane(s_last)) {
+          const int rslot = slot0 + run * kMergeGroup;
+          merge_partials<HD>(a, cu.request, qh0, rslot, 1, run_len, runs == 1 ? -1 : rslot);
+          if (threadIdx.x == 0) atomicExch(cnt + 1 + run, 0);   // ready for the next launch
+          if (runs > 1) {
+            wait_vector_memory();
+            lds_barrier();
+            if (threadIdx.x == 0) s_last = atomicAdd(cnt, 1) == runs - 1;
+            lds_barrier();
+            if (__builtin_amdgcn_readfirstlane(s_last)) {
+              merge_partials<HD>(a, cu.request, qh0, slot0, kMergeGroup, runs, -1);
+              if (threadIdx.x == 0) atomicExch(cnt, 0);
+            }
           }
         }
       }
+      load_q(nu);
+      itemv = load_item_lanes(a.items, min(nxt2, last_item), lane);
+      lds_barrier();                       // LDS free for the next unit
+      claimed = nxt < a.steal_limit;
+      cur = nxt;
+      cu = nu;
+      nxt = nxt2;
+      par ^= 1;
+      buf ^= 1;
     }
-    load_q(nu);
-    itemv = load_item_lanes(a.items, min(nxt2, last_item), lane);
-    lds_barrier();                       // LDS free for the next unit
-    cur = nxt;
-    cu = nu;
-    nxt = nxt2;
-    par ^= 1;
-    buf ^= 1;
+    // ---- the chain has run out: go on with a unit taken from another one
+    if (a.steal_limit == 0) break;
+    cur = steal();
+    if (cur < 0) break;
+    nxt = a.num_items;
+    claimed = false;
   }
   // The last workgroup out resets the counters for the next launch: every
   // other workgroup has already taken its final ticket by then.

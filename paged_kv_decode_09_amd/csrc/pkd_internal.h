@@ -22,6 +22,21 @@ constexpr int kMergeRowsPerBlock = 4;
 // kMergeGroup consecutive units of a (request, kv head) first, then the runs.
 constexpr int kMergeGroup = 8;
 
+// Reserve slots: the unit a decode workgroup holds beyond its current one is
+// published in one of its two slots (by unit parity) so that a workgroup
+// with no work left can take it. A slot value (unsigned) below kMaxItems is
+// a published unit, free to take. The owner claims it by adding kClaimStep
+// near the end of its current unit; a thief replaces the published value by
+// kStolen with a compare-and-swap. The owner sees kStolen in the value its
+// addition returns iff the thief came first. 0xFFFFFFFF: never published.
+// Only units of at least kStealMinBytes of K/V are published: a stolen unit
+// starts without prefetch and its owner spends a few microseconds dropping
+// it, which a short unit does not repay.
+constexpr uint32_t kMaxItems = 1u << 24;
+constexpr uint32_t kClaimStep = 1u << 25;
+constexpr uint32_t kStolen = 1u << 28;
+constexpr int64_t kStealMinBytes = 512 << 10;
+
 // Wavefronts per SIMD (= decode workgroups per compute unit) each decode
 // kernel instance is built for: its launch bounds cap its registers to fit,
 // and the planner sizes the launch for it. Two steps of K/V rows, the next
@@ -50,6 +65,9 @@ struct HostPlan {
   pkd_plan_params params{};
   pkd_plan_info info{};
   int32_t max_units = 0;   // most units of one request (per kv head)
+  // items [0, steal_limit) have at least kStealMinBytes of K/V (the items
+  // are sorted longest first): only these are published for stealing
+  int32_t steal_limit = 0;
   std::vector<pkd_work_item> items;
   std::vector<MergeRow> merges;
 };
@@ -81,6 +99,10 @@ struct DecodeArgs {
   // counters[0]: next item to take; counters[1]: workgroups finished. Both
   // are zero when a launch starts; the last workgroup to finish resets them.
   int32_t* counters;
+  // [2 * gridDim.x] reserve slots, two per workgroup (by unit parity): the
+  // unit a workgroup holds beyond its current one, for workgroups whose own
+  // units have run out (encoding at kMaxItems). 0xFFFFFFFF after planning.
+  int32_t* reserve;
   // [B][num_kv_heads][merge_stride] per (request, kv head) of a split
   // request: [0] runs merged, [1 + r] units of run r finished. Zero when a
   // launch starts; each is reset by the workgroup that completes it.
@@ -109,6 +131,7 @@ struct DecodeArgs {
   float cap;            // soft cap (> 0 only in the capped kernels)
   float inv_cap;
   float v_scale;
+  int32_t steal_limit;  // items below it may be published for stealing
 };
 
 struct MergeArgs {

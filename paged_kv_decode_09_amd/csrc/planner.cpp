@@ -251,8 +251,9 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
       }
     }
     if (split_req) partials += (int32_t)n;
-    if (units.size() > (size_t)(INT32_MAX / 2))
-      return fail(PKD_EUNSUPPORTED, "too many work units");
+    // unit indices are published in 24 bits (the reserve slots)
+    if (units.size() >= (size_t)kMaxItems)
+      return fail(PKD_EUNSUPPORTED, fmt("more than %u work units", kMaxItems - 1));
   }
 
   // ---- launch order: longest units first. The decode workgroups take
@@ -268,6 +269,14 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
   });
   out->items.resize(units.size());
   for (size_t k = 0; k < units.size(); ++k) out->items[k] = units[k].it;
+  const int64_t token_bytes = 2LL * p.head_dim * (p.kv_dtype == PKD_E4M3 ? 1 : 2);
+  out->steal_limit = 0;
+  while (out->steal_limit < (int32_t)units.size() &&
+         units[out->steal_limit].tokens * token_bytes >= kStealMinBytes)
+    ++out->steal_limit;
+  // The units held when workgroups start to run out of work are about the
+  // last nwg: if none of them is long enough, nothing is published at all.
+  if (out->steal_limit <= (int64_t)units.size() - nwg) out->steal_limit = 0;
 
   // the merge counters are addressed with 32-bit byte offsets
   if ((int64_t)B * p.num_kv_heads * (1 + (out->max_units + kMergeGroup - 1) / kMergeGroup) * 4 >

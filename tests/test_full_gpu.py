@@ -146,6 +146,22 @@ def test_window_zero_returns_last_row_bit_exactly():
         assert torch.equal(o[i], exp[i])
 
 
+@pytest.mark.parametrize("name", ["long_context", "fp8_kv"])
+def test_full_size_runs_repeat_bitwise(name):
+    """Workgroups that run out of units take long units that others hold in
+    reserve, so which workgroup runs a unit changes from run to run (these
+    two workloads publish units for that). A unit's arithmetic, and the
+    merge order of a split request, do not depend on it: every run gives
+    the same bits."""
+    w = wl.WORKLOADS[name]
+    say(name)
+    case = wl.make_case(w, device="cuda")
+    first, lfirst, plan = run_gpu(w, case)
+    for _ in range(8):
+        o, lse, _ = run_gpu(w, case, plan=plan)
+        assert torch.equal(o, first) and torch.equal(lse, lfirst)
+
+
 def test_fixed_split_is_deterministic_and_batch_invariant():
     w = wl.small_workload(seed=47, batch=5, num_qo_heads=64, num_kv_heads=8, head_dim=128,
                           lengths=("fixed", [5000, 70, 12000, 4096, 1]),
