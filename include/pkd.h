@@ -87,7 +87,7 @@ typedef struct {
 
 /* One unit of decode work: the tokens [token_begin, token_end) of one chunk of
  * one request, for one kv head and its G q heads. Under a fixed split, chunks
- * longer than 1024 tokens are processed as units of 1024 tokens cut at fixed
+ * longer than 2048 tokens are processed as units of 2048 tokens cut at fixed
  * offsets from the chunk start, so each unit depends on its request alone. */
 typedef struct {
   int32_t request;

@@ -56,7 +56,7 @@ constexpr int kMinUnitTokens = kUnitQuantum;
 // this many tokens (cut at fixed offsets from the chunk start), so that the
 // work can be spread over all workgroups. The cut depends only on the
 // request's own length, so results stay batch invariant.
-constexpr int kMaxUnitTokens = 1024;
+constexpr int kMaxUnitTokens = 2048;
 
 }  // namespace
 

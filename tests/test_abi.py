@@ -84,7 +84,7 @@ def test_run_before_plan_and_bad_merge_args_fail_on_host():
 
 # Under a fixed split, chunks are processed as units of at most this many
 # tokens, cut at fixed offsets from the chunk start.
-FIXED_UNIT_MAX = 1024
+FIXED_UNIT_MAX = 2048
 
 
 def unit_bounds(L, page_size, split, window, cap):
@@ -200,10 +200,10 @@ def test_named_workload_plans(name):
     coverage(items, w.num_kv_heads, pt.lengths, starts)
     assert 1 <= info.num_workgroups <= 256 * 4
     if name == "long_context":
-        # 80 chunks of 256 pages (4096 tokens), each processed as 4 units of
-        # 1024 tokens, for every kv head
-        assert info.split_pages == 256 and info.num_items == 80 * 4 * 8
-        assert info.num_partials == 80 * 4
+        # 80 chunks of 256 pages (4096 tokens), each processed as 2 units of
+        # 2048 tokens, for every kv head
+        assert info.split_pages == 256 and info.num_items == 80 * 2 * 8
+        assert info.num_partials == 80 * 2
 
 
 @pytest.mark.parametrize("name", ["serving_batch", "long_context", "gemma2_decode", "fp8_kv"])
