@@ -235,7 +235,7 @@ __device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t r, uint32
 template <int HD>
 __device__ void merge_partials(const DecodeArgs& a, int request, int qh0, int first, int stride,
                                int count, int out_slot) {
-  constexpr int kBatch = HD >= 128 ? 16 : 8;
+  constexpr int kBatch = HD == 128 ? 16 : 8;
   constexpr int cols4 = HD / 4;
   const int n = count;
   const int G = a.group;
@@ -512,6 +512,8 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
 
   // reserve slots of all workgroups, two each (by unit parity)
   const int nslots = 2 * (int)gridDim.x;
+  // the ticket counter (4 bytes)
+  const __amdgpu_buffer_rsrc_t cnt_rsrc = make_rsrc(a.counters, 4);
   const __amdgpu_buffer_rsrc_t res_rsrc = make_rsrc(a.reserve, (uint32_t)nslots * 4);
 
   // ---- Units form a pipeline per workgroup. While unit `cur` is attended,
@@ -519,7 +521,10 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   // last load issue of cur's step loop is nxt's first step, so that cur's
   // end-of-unit work (wavefront merge, outputs, merge of split requests)
   // overlaps with those loads. A workgroup holds at most one unit beyond
-  // the current one, plus the ticket it takes while the current one runs.
+  // the current one. It takes the ticket for the unit after that in the
+  // last pass of the current unit's steps, early enough for the ticket to
+  // return by the unit's end, late enough that near the end of the queue
+  // the last units go to the workgroups about to need them.
   // Its first two units are items blockIdx.x and blockIdx.x + gridDim.x
   // (the grid never exceeds the item count); later ones are tickets from
   // the plan's counter, offset by twice the grid size.
@@ -613,9 +618,9 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
     while (cur < a.num_items) {
       // ---- unit start: cur's first step is in flight in A, its q in bq, the
       // item of nxt in itemv
-      // the unit after nxt (none once the tickets are spent)
-      int tk = a.num_items;
-      if (threadIdx.x == 0 && nxt < a.num_items) tk = atomicAdd(&a.counters[0], 1);
+      // the ticket for the unit after nxt, taken by thread 0 in the last
+      // pass of cur's steps (none once the tickets are spent)
+      unsigned tk = 0;
       // nxt (read after cur's first step): its first page window (the first
       // kWaves*64 pages now, to LDS at cur's end; more, rarely, then), and the
       // pages of this wave's first step of nxt (for the hand-over issue)
@@ -699,6 +704,13 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
         int j = 1;
         do {
           issue(W, s0 + (j + 1) * kWaves, A);
+          {
+            // the ticket: in range for thread 0 in the last pass of the last
+            // window only (the other lanes and passes do nothing)
+            const uint32_t toff = j + 3 >= m2 && w1 == nsteps && nxt < a.num_items && threadIdx.x == 0
+                                      ? 0u : 0x80000000u;
+            tk = (unsigned)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, cnt_rsrc, toff, 0, 0);
+          }
           __builtin_amdgcn_sched_barrier(0);
           consume(W, s0 + j * kWaves, B);
           __builtin_amdgcn_sched_barrier(0);
@@ -737,7 +749,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
       if ((int)threadIdx.x < nwpages) s_pages[buf ^ 1][threadIdx.x] = pgn;
       for (int i = threadIdx.x + kWaves * 64; i < nwpages; i += kWaves * 64)
         s_pages[buf ^ 1][i] = npidx[Wn.wpage0 + i];
-      if (threadIdx.x == 0) s_ticket[par] = 2 * (int)gridDim.x + tk;
+      if (threadIdx.x == 0) s_ticket[par] = nxt < a.num_items ? 2 * (int)gridDim.x + (int)tk : a.num_items;
       d_run = wave_sum_over_groups(d_run);
       float* sacc = reinterpret_cast<float*>(vl);   // [16 heads][HD], own region
       if (n < group) {
