@@ -162,6 +162,46 @@ def test_full_size_runs_repeat_bitwise(name):
         assert torch.equal(o, first) and torch.equal(lse, lfirst)
 
 
+@pytest.mark.parametrize("name", ["serving_batch", "long_context"])
+def test_graph_replays_match_eager_runs(name):
+    """pkd_run only enqueues one launch, so a decode step can be captured in a
+    HIP graph. Two runs (two queries) are captured; every replay, with eager
+    runs, output clears and synchronisations between replays, must give the
+    eager bits, which also checks that the counters, reserve slots and merge
+    counters the kernel resets for the next launch are left ready."""
+    w = wl.WORKLOADS[name]
+    say(name, "graph")
+    case = wl.make_case(w, device="cuda")
+    q2 = torch.flip(case.q, dims=[0]).contiguous()
+    plan = plan_for(w, case)
+    ws = (torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+          if plan.workspace_bytes else None)
+    ref = []
+    for q in (case.q, q2):
+        o, lse = plan.run(q, case.pool, k_scale=w.k_scale, v_scale=w.v_scale,
+                          return_lse=True, workspace=ws)
+        ref.append((o.clone(), lse.clone()))
+    torch.cuda.synchronize()
+    outs = [(torch.empty_like(r[0]), torch.empty_like(r[1])) for r in ref]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for q, (o, lse) in zip((case.q, q2), outs):
+            plan.run(q, case.pool, k_scale=w.k_scale, v_scale=w.v_scale,
+                     out=o, lse=lse, workspace=ws)
+    for rep in range(4):
+        for o, lse in outs:
+            o.zero_()
+            lse.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (o, lse), (ro, rl) in zip(outs, ref):
+            assert torch.equal(o, ro) and torch.equal(lse, rl), rep
+        eo, el = plan.run(q2, case.pool, k_scale=w.k_scale, v_scale=w.v_scale,
+                          return_lse=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(eo, ref[1][0]) and torch.equal(el, ref[1][1]), rep
+
+
 def test_fixed_split_is_deterministic_and_batch_invariant():
     w = wl.small_workload(seed=47, batch=5, num_qo_heads=64, num_kv_heads=8, head_dim=128,
                           lengths=("fixed", [5000, 70, 12000, 4096, 1]),
