@@ -87,8 +87,10 @@ typedef struct {
 
 /* One unit of decode work: the tokens [token_begin, token_end) of one chunk of
  * one request, for one kv head and its G q heads. Under a fixed split, chunks
- * longer than 2048 tokens are processed as units of 2048 tokens cut at fixed
- * offsets from the chunk start, so each unit depends on its request alone. */
+ * longer than 3072 tokens are processed as units of 3072 tokens cut at fixed
+ * offsets from the chunk start, so each unit depends on its request alone.
+ * Under the planner's own split a request is cut into units of equal length
+ * (to the token), as few as keep each within split_pages pages. */
 typedef struct {
   int32_t request;
   int32_t kv_head;
@@ -105,7 +107,8 @@ typedef struct {
   int32_t num_workgroups;   /* decode workgroups; they take items in order  */
   int32_t num_split_requests; /* requests cut into more than one unit       */
   int32_t num_partials;     /* workspace slots (units of split requests)    */
-  int32_t split_pages;      /* chunk size in pages; 0 = no split            */
+  int32_t split_pages;      /* fixed split: chunk size in pages; planner's
+                               split: longest unit in pages; 0 = no split   */
   int32_t workgroups_per_cu; /* decode workgroups resident per compute unit */
   int64_t attended_tokens;  /* sum over requests of attended tokens         */
   size_t workspace_bytes;   /* bytes the workspace of pkd_run must hold     */

@@ -55,8 +55,10 @@ constexpr int kMinUnitTokens = kUnitQuantum;
 // Under a fixed split, chunks longer than this are processed as sub-chunks of
 // this many tokens (cut at fixed offsets from the chunk start), so that the
 // work can be spread over all workgroups. The cut depends only on the
-// request's own length, so results stay batch invariant.
-constexpr int kMaxUnitTokens = 2048;
+// request's own length, so results stay batch invariant. A chunk of 4096
+// tokens becomes a unit of 3072 and one of 1024: the short units, taken
+// last, even out the workgroups' ends better than two units of 2048.
+constexpr int kMaxUnitTokens = 3072;
 
 }  // namespace
 
@@ -213,6 +215,15 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
     std::vector<std::pair<int64_t, int64_t>> ranges;
     if (split <= 0) {
       ranges.emplace_back(r.start, r.kv_len);
+    } else if (p.fixed_split_size <= 0) {
+      // the planner's own split: the attended tokens in the fewest units of
+      // at most `split` pages, all of about the same length (units that
+      // differ less leave less for the longest-first order to even out)
+      const int64_t att = r.kv_len - r.start;
+      const int64_t cap = (int64_t)split * P;
+      const int64_t n = (att + cap - 1) / cap;
+      for (int64_t c = 0; c < n; ++c)
+        ranges.emplace_back(r.start + att * c / n, r.start + att * (c + 1) / n);
     } else {
       const int64_t chunk_tokens = (int64_t)split * P;
       const int64_t first = (r.start / P) / split;

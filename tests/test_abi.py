@@ -84,7 +84,7 @@ def test_run_before_plan_and_bad_merge_args_fail_on_host():
 
 # Under a fixed split, chunks are processed as units of at most this many
 # tokens, cut at fixed offsets from the chunk start.
-FIXED_UNIT_MAX = 2048
+FIXED_UNIT_MAX = 3072
 
 
 def unit_bounds(L, page_size, split, window, cap):
@@ -137,16 +137,26 @@ def test_split_chunks_tile_each_request(split, window):
     starts = [oracle.window_start(int(L), window) for L in lens]
     per = coverage(items, 4, lens, starts)
     if split == 0:
-        split = info.split_pages
-        cap = None
+        # the planner's split: each request in the fewest units of at most
+        # split_pages pages, of equal length to the token
+        cap_t = info.split_pages * 16
+
+        def bounds(L):
+            s0 = oracle.window_start(L, window)
+            if cap_t == 0:
+                return [(s0, L)]
+            n = -(-(L - s0) // cap_t)
+            return [(s0 + (L - s0) * c // n, s0 + (L - s0) * (c + 1) // n)
+                    for c in range(n)]
     else:
         assert info.split_pages == split
-        cap = FIXED_UNIT_MAX
+
+        def bounds(L):
+            return unit_bounds(L, 16, split, window, FIXED_UNIT_MAX)
     for (r, h), ch in per.items():
-        ref = unit_bounds(int(lens[r]), 16, split, window, cap)
-        assert [(c[1], c[2]) for c in ch] == ref
+        assert [(c[1], c[2]) for c in ch] == bounds(int(lens[r]))
     assert info.attended_tokens == sum(int(L) - s for L, s in zip(lens, starts))
-    nunits = [len(unit_bounds(int(L), 16, split, window, cap)) for L in lens]
+    nunits = [len(bounds(int(L))) for L in lens]
     assert info.num_split_requests == sum(1 for k in nunits if k > 1)
     parts = sum(k for k in nunits if k > 1)
     assert info.num_partials == parts
@@ -200,8 +210,8 @@ def test_named_workload_plans(name):
     coverage(items, w.num_kv_heads, pt.lengths, starts)
     assert 1 <= info.num_workgroups <= 256 * 4
     if name == "long_context":
-        # 80 chunks of 256 pages (4096 tokens), each processed as 2 units of
-        # 2048 tokens, for every kv head
+        # 80 chunks of 256 pages (4096 tokens), each processed as units of
+        # 3072 and 1024 tokens, for every kv head
         assert info.split_pages == 256 and info.num_items == 80 * 2 * 8
         assert info.num_partials == 80 * 2
 
