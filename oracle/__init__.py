@@ -18,6 +18,7 @@ from .oracle import (
     merge_states,
     decode_request_split,
     batch_decode_split,
+    batch_decode_multi,
 )
 
 __all__ = [
@@ -34,4 +35,5 @@ __all__ = [
     "merge_states",
     "decode_request_split",
     "batch_decode_split",
+    "batch_decode_multi",
 ]

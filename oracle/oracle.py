@@ -36,6 +36,13 @@ unless stated otherwise):
 * Split-KV (plan() parameter fixed_split_size, "in pages"): the sequence is
   cut into chunks of that many pages; per-chunk states are combined by a
   log-sum-exp merge (the merge_states step named there).
+* Several query tokens per request (run() parameter q_len_per_req, default
+  1). Readings taken: q, o and lse hold q_len_per_req consecutive rows per
+  request, in token order; query token j of a request sits at position
+  kv_len - q_len_per_req + j, the causal diagonal kv_len - qo_len of the
+  prefill mask example, so it attends tokens t <= that position (and, with a
+  window, t >= that position - window_left). Each query token is therefore
+  exactly a one-token decode over the prefix that ends at its position.
 """
 import math
 
@@ -275,4 +282,42 @@ def batch_decode_split(q, paged_kv_cache, layout: str, indptr, indices,
         o[r], lse[r] = decode_request_split(
             q[i], K, V, q_dtype, kv_dtype, sm_scale, page_size, split_pages,
             logits_soft_cap, window_left, q_scale, k_scale, v_scale)
+    return o, lse
+
+
+def batch_decode_multi(q, paged_kv_cache, layout: str, indptr, indices,
+                       last_page_len, page_size: int, q_len_per_req: int,
+                       q_dtype: str, kv_dtype: str, sm_scale: float,
+                       logits_soft_cap: float = 0.0, window_left: int = -1,
+                       q_scale: float = 1.0, k_scale: float = 1.0,
+                       v_scale: float = 1.0, requests=None):
+    """Decode with q_len_per_req query tokens per request, fp64.
+
+    ``q`` is [batch * q_len_per_req, num_qo_heads, head_dim] (request-major,
+    tokens in order). Returns o [len(requests) * q_len_per_req, num_qo_heads,
+    head_dim] and lse [len(requests) * q_len_per_req, num_qo_heads]. Query
+    token j of request i is the one-token decode of the prefix of length
+    kv_len - q_len_per_req + j + 1.
+    """
+    Q = int(q_len_per_req)
+    if Q < 1:
+        raise ValueError("q_len_per_req must be >= 1")
+    k_cache, v_cache = _cache_pair(paged_kv_cache)
+    lens = kv_lengths(indptr, last_page_len, page_size)
+    if np.any(lens < Q):
+        raise ValueError("every request needs kv_len >= q_len_per_req")
+    reqs = range(len(lens)) if requests is None else list(requests)
+    nq, hd = q.shape[1], q.shape[2]
+    o = np.zeros((len(reqs) * Q, nq, hd))
+    lse = np.zeros((len(reqs) * Q, nq))
+    for r, i in enumerate(reqs):
+        L = int(lens[i])
+        K, V = gather_request(k_cache, v_cache, layout, indices, indptr, i, L,
+                              page_size)
+        for j in range(Q):
+            pos = L - Q + j
+            o[r * Q + j], lse[r * Q + j] = decode_request(
+                q[i * Q + j], K[:pos + 1], V[:pos + 1], q_dtype, kv_dtype,
+                sm_scale, logits_soft_cap, window_left, q_scale, k_scale,
+                v_scale)
     return o, lse

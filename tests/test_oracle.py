@@ -402,3 +402,117 @@ def test_poison_fills_only_unreadable_slots():
     # everything not gathered is NaN
     total = pool[:, 0, :, 0, 0].size
     assert np.isnan(pool[:, 0, :, 0, 0]).sum() == total - seen
+
+
+# ------------------------------------------- several query tokens per request
+
+def sdpa_masked(q_rows, K, V, sm_scale, mask):
+    """torch SDPA (fp64, CPU) of query rows [Q, nq, hd] over K/V [L, nkv, hd]
+    with a boolean mask [Q, L] (True = attend), grouped heads expanded."""
+    qt = torch.from_numpy(np.ascontiguousarray(q_rows.transpose(1, 0, 2)))[None]
+    kt = torch.from_numpy(np.ascontiguousarray(K.transpose(1, 0, 2)))[None]
+    vt = torch.from_numpy(np.ascontiguousarray(V.transpose(1, 0, 2)))[None]
+    m = torch.from_numpy(mask)[None, None]
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=sm_scale,
+                                       enable_gqa=True)
+    return o[0].numpy().transpose(1, 0, 2)
+
+
+def prefill_causal_mask(qo_len, kv_len, window_left=-1):
+    """The custom-mask construction of the prefill wrapper's example on the
+    decode API page (lower triangle with diagonal kv_len - qo_len), with the
+    inclusive left window cut out below it."""
+    m = torch.tril(torch.full((qo_len, kv_len), True),
+                   diagonal=kv_len - qo_len)
+    if window_left >= 0:
+        m &= torch.triu(torch.full((qo_len, kv_len), True),
+                        diagonal=kv_len - qo_len - window_left)
+    return m.numpy()
+
+
+@pytest.mark.parametrize("Q,group", [(2, 1), (3, 2), (4, 4), (8, 2), (16, 1)])
+@pytest.mark.parametrize("page_size", [1, 4, 16])
+def test_multi_token_matches_sdpa_with_the_prefill_causal_mask(Q, group,
+                                                              page_size):
+    rng = np.random.default_rng(Q * 100 + group * 10 + page_size)
+    nkv, hd = 2, 8
+    nq = nkv * group
+    lengths = [Q, Q + 1, int(rng.integers(Q, 45)), 37]
+    K = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    V = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    q = rng.standard_normal((len(lengths) * Q, nq, hd))
+    npages = sum((L + page_size - 1) // page_size for L in lengths)
+    for layout in ("NHD", "HND"):
+        cache, indptr, indices, last = scatter_to_pages(
+            K, V, layout, page_size, npages + 2, rng)
+        o, lse = oracle.batch_decode_multi(q, cache, layout, indptr, indices,
+                                           last, page_size, Q, "f64", "f64",
+                                           0.35)
+        for i, L in enumerate(lengths):
+            ref = sdpa_masked(q[i * Q:(i + 1) * Q], K[i], V[i], 0.35,
+                              prefill_causal_mask(Q, L))
+            assert np.max(np.abs(o[i * Q:(i + 1) * Q] - ref)) < 1e-12
+
+
+@pytest.mark.parametrize("window", [0, 1, 3, 10, 100])
+def test_multi_token_window_matches_sdpa(window):
+    rng = np.random.default_rng(window + 5)
+    Q, nkv, group, hd = 4, 2, 2, 8
+    lengths = [4, 5, 23, 40]
+    K = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    V = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    q = rng.standard_normal((len(lengths) * Q, nkv * group, hd))
+    cache, indptr, indices, last = scatter_to_pages(K, V, "NHD", 4, 40, rng)
+    o, _ = oracle.batch_decode_multi(q, cache, "NHD", indptr, indices, last, 4,
+                                     Q, "f64", "f64", 0.3, window_left=window,
+                                     logits_soft_cap=0.0)
+    for i, L in enumerate(lengths):
+        ref = sdpa_masked(q[i * Q:(i + 1) * Q], K[i], V[i], 0.3,
+                          prefill_causal_mask(Q, L, window))
+        assert np.max(np.abs(o[i * Q:(i + 1) * Q] - ref)) < 1e-12
+
+
+def test_multi_token_zero_query_counts_each_tokens_prefix():
+    # q = 0: every visible logit is 0, so lse of query token j is the log of
+    # the number of tokens it sees: min(L - Q + j + 1, window + 1).
+    rng = np.random.default_rng(3)
+    Q, nkv, hd = 3, 2, 4
+    lengths = [3, 9, 30]
+    K = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    V = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    cache, indptr, indices, last = scatter_to_pages(K, V, "HND", 2, 30, rng)
+    for window in (-1, 0, 4):
+        q = np.zeros((len(lengths) * Q, nkv, hd))
+        _, lse = oracle.batch_decode_multi(q, cache, "HND", indptr, indices,
+                                           last, 2, Q, "f64", "f64", 1.0,
+                                           window_left=window)
+        for i, L in enumerate(lengths):
+            for j in range(Q):
+                seen = L - Q + j + 1
+                if window >= 0:
+                    seen = min(seen, window + 1)
+                assert np.allclose(lse[i * Q + j], math.log(seen), atol=1e-12)
+
+
+def test_multi_token_last_token_is_the_single_token_decode():
+    rng = np.random.default_rng(8)
+    Q, nkv, hd = 4, 2, 8
+    lengths = [4, 19, 33]
+    K = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    V = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    q = rng.standard_normal((len(lengths) * Q, 2 * nkv, hd))
+    cache, indptr, indices, last = scatter_to_pages(K, V, "NHD", 4, 20, rng)
+    o, lse = oracle.batch_decode_multi(q, cache, "NHD", indptr, indices, last,
+                                       4, Q, "f64", "f64", 0.2)
+    o1, lse1 = oracle.batch_decode(q[Q - 1::Q], cache, "NHD", indptr, indices,
+                                   last, 4, "f64", "f64", 0.2)
+    assert np.array_equal(o[Q - 1::Q], o1) and np.array_equal(lse[Q - 1::Q], lse1)
+
+
+def test_multi_token_rejects_short_requests():
+    rng = np.random.default_rng(1)
+    K = [rng.standard_normal((2, 1, 4))]
+    cache, indptr, indices, last = scatter_to_pages(K, K, "NHD", 4, 2, rng)
+    with pytest.raises(ValueError):
+        oracle.batch_decode_multi(np.zeros((3, 1, 4)), cache, "NHD", indptr,
+                                  indices, last, 4, 3, "f64", "f64", 1.0)
