@@ -54,16 +54,17 @@ def algorithmic_bytes(w, pt):
     read once per kv head), q, o, fp32 lse, the page indices of the touched
     pages, indptr and last_page_len."""
     B, nq, nkv, hd = w.batch, w.num_qo_heads, w.num_kv_heads, w.head_dim
-    ps = w.page_size
+    ps, Q = w.page_size, w.q_len_per_req
     attended, touched = 0, 0
     for i in range(B):
         L = int(pt.lengths[i])
-        s0 = 0 if w.window_left < 0 else max(0, L - 1 - w.window_left)
+        # the union of the Q query tokens' windows (the first token's is widest)
+        s0 = 0 if w.window_left < 0 else max(0, L - Q - w.window_left)
         attended += L - s0
         touched += (L - 1) // ps - s0 // ps + 1
     kv = attended * nkv * hd * 2 * ELEM[w.kv_dtype]
-    q = B * nq * hd * ELEM[w.q_dtype]
-    out = B * nq * (hd * ELEM[w.o_dtype] + 4)
+    q = B * Q * nq * hd * ELEM[w.q_dtype]
+    out = B * Q * nq * (hd * ELEM[w.o_dtype] + 4)
     meta = touched * 4 + (B + 1) * 4 + B * 4
     return kv + q + out + meta
 
@@ -91,12 +92,17 @@ def run_cpu_baseline(w, case, budget_s=10.0):
     done, elapsed, nbytes, tokens = [], 0.0, 0, 0
     kw = dict(logits_soft_cap=w.logits_soft_cap, window_left=w.window_left,
               k_scale=w.k_scale, v_scale=w.v_scale)
+    Q = w.q_len_per_req
     for i in order:
         pool, indptr, indices, last = _sub_pool(case, [i])
-        qn = wl.raw_numpy(case.q[i:i + 1], w.q_dtype)
+        qn = wl.raw_numpy(case.q[i * Q:(i + 1) * Q], w.q_dtype)
         pn = wl.raw_numpy(pool, w.kv_dtype)
         t = time.perf_counter()
-        if w.fixed_split_size:
+        if Q > 1:
+            oracle.batch_decode_multi(qn, pn, w.layout, indptr, indices, last,
+                                      w.page_size, Q, w.q_dtype, w.kv_dtype,
+                                      w.sm_scale, **kw)
+        elif w.fixed_split_size:
             oracle.batch_decode_split(qn, pn, w.layout, indptr, indices, last,
                                       w.page_size, w.q_dtype, w.kv_dtype,
                                       w.sm_scale, w.fixed_split_size, **kw)
@@ -106,14 +112,14 @@ def run_cpu_baseline(w, case, budget_s=10.0):
                                 **kw)
         elapsed += time.perf_counter() - t
         L = int(case.pt.lengths[i])
-        s0 = 0 if w.window_left < 0 else max(0, L - 1 - w.window_left)
+        s0 = 0 if w.window_left < 0 else max(0, L - Q - w.window_left)
         tokens += L - s0
         done.append(i)
         if elapsed >= budget_s:
             break
     kvb = tokens * w.num_kv_heads * w.head_dim * 2 * ELEM[w.kv_dtype]
-    other = len(done) * w.num_qo_heads * w.head_dim * (
-        ELEM[w.q_dtype] + ELEM[w.o_dtype]) + len(done) * w.num_qo_heads * 4
+    other = len(done) * Q * w.num_qo_heads * (w.head_dim * (
+        ELEM[w.q_dtype] + ELEM[w.o_dtype]) + 4)
     gbs = (kvb + other) / elapsed / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads),
             "kind": "oracle",
@@ -173,11 +179,13 @@ def main():
         w.num_kv_heads, w.head_dim, w.page_size, kv_layout=w.layout,
         window_left=w.window_left, logits_soft_cap=w.logits_soft_cap or None,
         q_data_type=w.q_dtype, kv_data_type=w.kv_dtype, o_data_type=w.o_dtype,
-        sm_scale=w.sm_scale, fixed_split_size=w.fixed_split_size or None)
+        sm_scale=w.sm_scale, fixed_split_size=w.fixed_split_size or None,
+        q_len_per_req=w.q_len_per_req)
     info = plan.info
-    o = torch.empty((w.batch, w.num_qo_heads, w.head_dim),
+    rows = w.batch * w.q_len_per_req
+    o = torch.empty((rows, w.num_qo_heads, w.head_dim),
                     dtype=wl.TORCH_DTYPES[w.o_dtype], device=dev)
-    lse = torch.empty((w.batch, w.num_qo_heads), dtype=torch.float32,
+    lse = torch.empty((rows, w.num_qo_heads), dtype=torch.float32,
                       device=dev)
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8,
                      device=dev)
@@ -273,6 +281,7 @@ def main():
             "logits_soft_cap": w.logits_soft_cap,
             "window_left": w.window_left,
             "fixed_split_size": w.fixed_split_size,
+            "q_len_per_req": w.q_len_per_req,
             "split_pages_used": info.split_pages,
             "work_items": info.num_items,
             "attended_tokens": int(info.attended_tokens),

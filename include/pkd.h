@@ -22,6 +22,12 @@
  *   logits   x = sm_scale*q_scale*k_scale * (q . k); if logits_soft_cap > 0,
  *            x <- cap*tanh(x/cap)
  *   o        sum_t softmax(x)_t * v_scale * v_t ;  lse = ln sum_t exp(x_t)
+ *   Q        q_len_per_req (run() parameter of the same wrapper, default 1):
+ *            query tokens per request. q, o and lse then hold Q consecutive
+ *            rows per request, in token order; query token j sits at
+ *            position L_i-Q+j (the causal diagonal kv_len-qo_len of the
+ *            prefill wrapper's mask example) and attends t <= L_i-Q+j, and
+ *            with a window also t >= L_i-Q+j-window_left
  *
  * Memory and streams.
  *   Every device buffer (q, caches, indices, o, lse, workspace) is owned by
@@ -45,7 +51,7 @@
 extern "C" {
 #endif
 
-#define PKD_ABI_VERSION 2
+#define PKD_ABI_VERSION 3
 
 typedef enum {
   PKD_OK = 0,
@@ -83,10 +89,14 @@ typedef struct {
   int32_t window_left;      /* -1: whole sequence; >= 0: inclusive window   */
   int32_t fixed_split_size; /* pages per chunk; 0: the planner chooses      */
   int32_t disable_split_kv; /* nonzero: exactly one chunk per request       */
+  int32_t q_len_per_req;    /* Q, query tokens per request; 0 means 1;
+                               G*Q <= 16 and every L_i >= Q                 */
 } pkd_plan_params;
 
 /* One unit of decode work: the tokens [token_begin, token_end) of one chunk of
- * one request, for one kv head and its G q heads. Under a fixed split, chunks
+ * one request, for one kv head and its G q heads (and the Q query tokens).
+ * Tokens past a query token's position, or before its window, are masked
+ * for that token only. Under a fixed split, chunks
  * longer than 3072 tokens are processed as units of 3072 tokens cut at fixed
  * offsets from the chunk start, so each unit depends on its request alone.
  * Under the planner's own split a request is cut into units of equal length
@@ -100,6 +110,8 @@ typedef struct {
   int32_t partial;          /* -1: writes o/lse; else its workspace slot    */
   int32_t chunk;            /* unit index within the request (ascending)    */
   int32_t num_chunks;       /* units of the request per kv head (1: unsplit) */
+  int32_t query_pos;        /* position of the request's first query token,
+                               L_i - Q                                      */
 } pkd_work_item;
 
 typedef struct {
@@ -155,7 +167,7 @@ pkd_status pkd_plan_get_info(const pkd_plan* plan, pkd_plan_info* info);
 void pkd_plan_destroy(pkd_plan* plan);
 
 /* run() (flashinfer.decode › BatchDecodeWithPagedKVCacheWrapper › run()):
- *   q        device, [B][num_qo_heads][head_dim] in q_dtype, contiguous
+ *   q        device, [B*Q][num_qo_heads][head_dim] in q_dtype, contiguous
  *   k_cache  device, K pages in kv_dtype and the plan's layout
  *   v_cache  device, V pages; for the 5-D cache [pages][2][...] pass
  *            v_cache = k_cache + P*num_kv_heads*head_dim elements
@@ -163,8 +175,8 @@ void pkd_plan_destroy(pkd_plan* plan);
  *            2*P*num_kv_heads*head_dim for the 5-D cache,
  *            P*num_kv_heads*head_dim for a (k_cache, v_cache) pair
  *   q_scale, k_scale, v_scale  calibration scales (1.0 = none)
- *   o        device, [B][num_qo_heads][head_dim] in o_dtype, written
- *   lse      device, [B][num_qo_heads] fp32 natural-log LSE, or NULL
+ *   o        device, [B*Q][num_qo_heads][head_dim] in o_dtype, written
+ *   lse      device, [B*Q][num_qo_heads] fp32 natural-log LSE, or NULL
  *   workspace, workspace_bytes  device scratch of at least
  *            pkd_plan_info.workspace_bytes (may be NULL when that is 0); its
  *            contents need no initialisation

@@ -18,7 +18,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkd.so")
-ABI_VERSION = 2            # PKD_ABI_VERSION of include/pkd.h
+ABI_VERSION = 3            # PKD_ABI_VERSION of include/pkd.h
 
 PKD_OK, PKD_EINVAL, PKD_EUNSUPPORTED, PKD_EHIP, PKD_ENOMEM, PKD_EWORKSPACE = (
     0, -1, -2, -3, -4, -5)
@@ -44,14 +44,16 @@ class pkd_plan_params(ctypes.Structure):
                 ("logits_soft_cap", ctypes.c_float),
                 ("window_left", ctypes.c_int32),
                 ("fixed_split_size", ctypes.c_int32),
-                ("disable_split_kv", ctypes.c_int32)]
+                ("disable_split_kv", ctypes.c_int32),
+                ("q_len_per_req", ctypes.c_int32)]
 
 
 class pkd_work_item(ctypes.Structure):
     _fields_ = [("request", ctypes.c_int32), ("kv_head", ctypes.c_int32),
                 ("token_begin", ctypes.c_int32), ("token_end", ctypes.c_int32),
                 ("page_base", ctypes.c_int32), ("partial", ctypes.c_int32),
-                ("chunk", ctypes.c_int32), ("num_chunks", ctypes.c_int32)]
+                ("chunk", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
+                ("query_pos", ctypes.c_int32)]
 
 
 class pkd_plan_info(ctypes.Structure):
@@ -151,7 +153,7 @@ def make_params(batch_size, num_qo_heads, num_kv_heads, head_dim, page_size,
                 kv_layout="NHD", window_left=-1, logits_soft_cap=None,
                 q_data_type=torch.float16, kv_data_type=None,
                 o_data_type=None, sm_scale=None, fixed_split_size=None,
-                disable_split_kv=False) -> pkd_plan_params:
+                disable_split_kv=False, q_len_per_req=1) -> pkd_plan_params:
     q_code = _dtype_code(q_data_type)
     kv_code = q_code if kv_data_type is None else _dtype_code(kv_data_type)
     o_code = q_code if o_data_type is None else _dtype_code(o_data_type)
@@ -167,7 +169,8 @@ def make_params(batch_size, num_qo_heads, num_kv_heads, head_dim, page_size,
         logits_soft_cap=0.0 if not logits_soft_cap else logits_soft_cap,
         window_left=int(window_left),
         fixed_split_size=0 if not fixed_split_size else int(fixed_split_size),
-        disable_split_kv=int(bool(disable_split_kv)))
+        disable_split_kv=int(bool(disable_split_kv)),
+        q_len_per_req=1 if q_len_per_req is None else int(q_len_per_req))
 
 
 def plan_query(indptr, last_page_len, num_cus: int = 256, **kw):
@@ -225,7 +228,8 @@ class PagedDecodePlan:
                  q_data_type=torch.float16, kv_data_type=None,
                  o_data_type=None, sm_scale: Optional[float] = None,
                  fixed_split_size: Optional[int] = None,
-                 disable_split_kv: bool = False, stream=None):
+                 disable_split_kv: bool = False, stream=None,
+                 q_len_per_req: int = 1):
         self._handle = None
         ip, lp = _host_i32(indptr), _host_i32(last_page_len)
         if indices.dtype != torch.int32 or not indices.is_cuda:
@@ -234,7 +238,7 @@ class PagedDecodePlan:
                                   page_size, kv_layout, window_left,
                                   logits_soft_cap, q_data_type, kv_data_type,
                                   o_data_type, sm_scale, fixed_split_size,
-                                  disable_split_kv)
+                                  disable_split_kv, q_len_per_req)
         self.indices = indices.contiguous()   # borrowed by the plan: keep alive
         h = _P()
         _check(lib().pkd_plan_create(ctypes.byref(self.params), ip.ctypes.data,
@@ -256,7 +260,9 @@ class PagedDecodePlan:
     def _args(self, q, paged_kv_cache, q_scale, k_scale, v_scale, out, lse,
               return_lse, workspace):
         p = self.params
-        B, nq, hd = p.batch_size, p.num_qo_heads, p.head_dim
+        # q, o and lse hold q_len_per_req rows per request
+        B = p.batch_size * max(1, p.q_len_per_req)
+        nq, hd = p.num_qo_heads, p.head_dim
         if tuple(q.shape) != (B, nq, hd) or not q.is_contiguous():
             raise PkdError(PKD_EINVAL, f"q must be contiguous [{B}, {nq}, {hd}]")
         if _dtype_code(q.dtype) != p.q_dtype:
@@ -274,6 +280,10 @@ class PagedDecodePlan:
             raise PkdError(PKD_EINVAL, "out has the wrong shape or dtype")
         if return_lse and lse is None:
             lse = torch.empty((B, nq), dtype=torch.float32, device=q.device)
+        elif lse is not None and (tuple(lse.shape) != (B, nq) or
+                                  lse.dtype != torch.float32 or
+                                  not lse.is_contiguous()):
+            raise PkdError(PKD_EINVAL, f"lse must be contiguous fp32 [{B}, {nq}]")
         ws_bytes = self.workspace_bytes
         if workspace is None and ws_bytes > 0:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
@@ -286,7 +296,8 @@ class PagedDecodePlan:
     def run(self, q: torch.Tensor, paged_kv_cache, q_scale=None, k_scale=None,
             v_scale=None, out=None, lse=None, return_lse: bool = False,
             workspace: Optional[torch.Tensor] = None, stream=None):
-        """o [B, num_qo_heads, head_dim], or (o, lse) when return_lse."""
+        """o [B * q_len_per_req, num_qo_heads, head_dim], or (o, lse) when
+        return_lse."""
         (q, kp, vp, stride, sc, out, lse, ws_ptr, ws_len,
          _ws) = self._args(q, paged_kv_cache, q_scale, k_scale, v_scale, out,
                            lse, return_lse or lse is not None, workspace)
@@ -320,7 +331,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
              kv_data_type=None, o_data_type=None, data_type=None,
              sm_scale=None, rope_scale=None, rope_theta=None,
              non_blocking=True, fixed_split_size=None,
-             disable_split_kv=False) -> None:
+             disable_split_kv=False, q_len_per_req=1) -> None:
         if pos_encoding_mode != "NONE":
             raise PkdError(PKD_EUNSUPPORTED,
                            f"pos_encoding_mode {pos_encoding_mode!r}")
@@ -331,16 +342,20 @@ class BatchDecodeWithPagedKVCacheWrapper:
             indptr, indices.to(torch.int32), last_page_len, num_qo_heads,
             num_kv_heads, head_dim, page_size, self._layout, window_left,
             logits_soft_cap, q_data_type, kv_data_type, o_data_type, sm_scale,
-            fixed_split_size, disable_split_kv)
+            fixed_split_size, disable_split_kv, q_len_per_req=q_len_per_req)
         need = self._plan.workspace_bytes
         if self._ws.numel() * self._ws.element_size() < need:
             self._ws = torch.empty(need, dtype=torch.uint8,
                                    device=self._ws.device)
 
     def run(self, q, paged_kv_cache, q_scale=None, k_scale=None, v_scale=None,
-            out=None, lse=None, return_lse=False):
+            out=None, lse=None, return_lse=False, q_len_per_req=None):
         if self._plan is None:
             raise PkdError(PKD_EINVAL, "run() before plan()")
+        planned = max(1, self._plan.params.q_len_per_req)
+        if q_len_per_req is not None and int(q_len_per_req) != planned:
+            raise PkdError(PKD_EINVAL, f"q_len_per_req {q_len_per_req} differs "
+                           f"from the plan's {planned}")
         ws = self._ws if self._plan.workspace_bytes > 0 else None
         return self._plan.run(q, paged_kv_cache, q_scale, k_scale, v_scale,
                               out, lse, return_lse, ws)

@@ -233,10 +233,11 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
   a.lse = lse;
   const int32_t parts = plan->host.info.num_partials;
   a.ws_o = reinterpret_cast<float*>(workspace);
-  a.ws_o_bytes = (size_t)parts * p.num_qo_heads * p.head_dim * 4;
+  const int32_t Q = pkd::q_len_of(p);
+  a.ws_o_bytes = (size_t)parts * Q * p.num_qo_heads * p.head_dim * 4;
   a.ws_lse = parts > 0 ? reinterpret_cast<float*>(
                              reinterpret_cast<char*>(workspace) +
-                             pkd::workspace_lse_offset(parts, p.num_qo_heads, p.head_dim))
+                             pkd::workspace_lse_offset(parts, Q * p.num_qo_heads, p.head_dim))
                        : nullptr;
   a.page_stride = page_stride;
   if (p.layout == PKD_NHD) {
@@ -249,6 +250,9 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
   a.num_qo_heads = p.num_qo_heads;
   a.num_kv_heads = p.num_kv_heads;
   a.group = p.num_qo_heads / p.num_kv_heads;
+  a.q_len = Q;
+  a.cols = a.group * Q;
+  a.window_left = p.window_left;
   int lg = 0;
   while ((1 << lg) < p.page_size) ++lg;
   a.log2_page = lg;

@@ -240,15 +240,19 @@ __device__ void merge_partials(const DecodeArgs& a, int request, int qh0, int fi
   const int n = count;
   const int G = a.group;
   const int nq = a.num_qo_heads;
+  const int R = a.q_len * nq;                          // query rows of a slot
   const size_t span = (size_t)(n - 1) * stride + 1;   // slots covered
   const __amdgpu_buffer_rsrc_t ro =
-      make_rsrc(a.ws_o + (size_t)first * nq * HD, (uint32_t)(span * nq * HD * 4));
+      make_rsrc(a.ws_o + (size_t)first * R * HD, (uint32_t)(span * R * HD * 4));
   const __amdgpu_buffer_rsrc_t rl =
-      make_rsrc(a.ws_lse + (size_t)first * nq, (uint32_t)(span * nq * 4));
-  for (int e0 = 0; e0 < G * cols4; e0 += kWaves * 64) {
+      make_rsrc(a.ws_lse + (size_t)first * R, (uint32_t)(span * R * 4));
+  for (int e0 = 0; e0 < a.cols * cols4; e0 += kWaves * 64) {
     const int e = e0 + (int)threadIdx.x;
-    const bool active = e < G * cols4;
+    const bool active = e < a.cols * cols4;
+    // row h of the unit: query token qj, q head qh0 + gh
     const int h = active ? e / cols4 : 0, c4 = active ? e - h * cols4 : 0;
+    const int qj = h / G, gh = h - qj * G;
+    const int row = qj * nq + qh0 + gh;                 // within a slot
     float M = -INFINITY, den = 0.0f;
     f32x4 num = {0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < n; k0 += kBatch) {
@@ -257,8 +261,8 @@ __device__ void merge_partials(const DecodeArgs& a, int request, int qh0, int fi
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const int k = min(k0 + j, n - 1) * stride;
-        x[j] = load_coherent4(ro, (uint32_t)((k * nq + qh0 + h) * HD + 4 * c4) * 4);
-        l[j] = load_coherent1(rl, (uint32_t)(k * nq + qh0 + h) * 4);
+        x[j] = load_coherent4(ro, (uint32_t)((k * R + row) * HD + 4 * c4) * 4);
+        l[j] = load_coherent1(rl, (uint32_t)(k * R + row) * 4);
       }
       float bm = -INFINITY;
 #pragma unroll
@@ -288,29 +292,31 @@ __device__ void merge_partials(const DecodeArgs& a, int request, int qh0, int fi
     if (!active) continue;
     const float lse2 = den > 0.0f ? M + __builtin_amdgcn_logf(den) : -INFINITY;
     if (out_slot < 0) {
-      const size_t orow = (size_t)request * nq + qh0 + h;
+      const size_t orow = ((size_t)request * a.q_len + qj) * nq + qh0 + gh;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         store_out(a.o, orow * HD + 4 * c4 + i, den > 0.0f ? num[i] / den : 0.0f, a.o_bf16);
       if (a.lse != nullptr && c4 == 0) a.lse[orow] = lse2 * kLn2;
     } else {
-      float* orow = a.ws_o + ((size_t)out_slot * nq + qh0 + h) * HD + 4 * c4;
+      float* orow = a.ws_o + ((size_t)out_slot * R + row) * HD + 4 * c4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) store_coherent(orow + i, den > 0.0f ? num[i] / den : 0.0f);
-      if (c4 == 0) store_coherent(a.ws_lse + (size_t)out_slot * nq + qh0 + h, lse2);
+      if (c4 == 0) store_coherent(a.ws_lse + (size_t)out_slot * R + row, lse2);
     }
   }
 }
 
 // Wave-uniform description of one work item (a pkd_work_item in SGPRs).
 struct Unit {
-  int request, kv_head, tb, te, page_base, partial, chunk, num_chunks;
+  int request, kv_head, tb, te, page_base, partial, chunk, num_chunks, qpos;
 };
 
-// Each lane loads dword (lane % 8) of item k: the whole item is then in
-// lanes 0..7 of one VGPR, in flight like any other vector load.
+// Lane l < 9 loads dword l of item k (lanes past it load the last one
+// again): the whole item is then in lanes 0..8 of one VGPR, in flight like
+// any other vector load.
+constexpr int kItemWords = sizeof(pkd_work_item) / 4;
 __device__ __forceinline__ unsigned load_item_lanes(const pkd_work_item* items, int k, int lane) {
-  return reinterpret_cast<const unsigned*>(items + k)[lane & 7];
+  return reinterpret_cast<const unsigned*>(items + k)[lane < kItemWords ? lane : kItemWords - 1];
 }
 __device__ __forceinline__ Unit unit_from_lanes(unsigned v) {
   Unit u;
@@ -322,6 +328,7 @@ __device__ __forceinline__ Unit unit_from_lanes(unsigned v) {
   u.partial = __builtin_amdgcn_readlane((int)v, 5);
   u.chunk = __builtin_amdgcn_readlane((int)v, 6);
   u.num_chunks = __builtin_amdgcn_readlane((int)v, 7);
+  u.qpos = __builtin_amdgcn_readlane((int)v, 8);
   return u;
 }
 
@@ -406,21 +413,29 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
     issue_rows(W, c0, c1, W.sp[(c0 >> lp) - W.wpage0], W.sp[(c1 >> lp) - W.wpage0], st);
   };
 
-  // q operand: head n of the unit's kv head. Columns n >= G load head 0
-  // again: they produce a duplicate of head 0's softmax that stays in its own
-  // columns (no step mixes columns) and is never written out. Every lane
-  // loads, so that the number of loads in flight is the same on every path.
+  // q operand: column n is query row n of the unit (query token n / G, q
+  // head n % G of the kv head). Columns n >= G*Q load row 0 again: they
+  // produce a duplicate of row 0's softmax that stays in its own columns (no
+  // step mixes columns) and is never written out. Every lane loads, so that
+  // the number of loads in flight is the same on every path.
+  const int cols = a.cols;
+  const int col_tok = (n < cols ? n : 0) / group;   // query token of column n
+  const int col_head = (n < cols ? n : 0) - col_tok * group;
   v8 bq[G_::kQkMfma];
   auto load_q = [&](const Unit& u) {
     const _Float16* qrow = reinterpret_cast<const _Float16*>(a.q) +
-                           ((size_t)u.request * a.num_qo_heads + u.kv_head * group + (n < group ? n : 0)) * HD;
+                           (((size_t)u.request * a.q_len + col_tok) * a.num_qo_heads +
+                            u.kv_head * group + col_head) * HD;
 #pragma unroll
     for (int j = 0; j < G_::kQkMfma; ++j)
       bq[j] = __builtin_bit_cast(v8, *reinterpret_cast<const u32x4*>(qrow + qk_hd<KV8>(j, g)));
   };
 
-  float m_run, d_run;     // running max (base-2 logits) / this lane's sum, head n
+  float m_run, d_run;     // running max (base-2 logits) / this lane's sum, column n
   f32x4 acc[G_::kPvMfma];
+  // Tokens column n may see in the current unit: up to its query token's
+  // position, and from its window start (set per unit).
+  int col_lo = 0, col_hi = 0;
 
   // Attend step s of window W whose K/V rows are in st. A step wholly past
   // the window (the padding step of an odd count) changes nothing.
@@ -452,6 +467,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
       *reinterpret_cast<u32x4*>(vl + tau1 * G_::kVPitch + 64 * p + 16 * g) = st.v[1][p];
     }
     // ---- online softmax (base 2)
+    const int lo = max(W.wlo, col_lo), hi = min(W.whi, col_hi);
     float x[8];
     float mx = -INFINITY;
 #pragma unroll
@@ -461,7 +477,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
         float v = sc[tile][i] * a.logit_scale;
         if constexpr (CAP) v = a.cap * tanh_from_exp(v * a.inv_cap) * kLog2e;
         const int t = t0 + 8 * g + 4 * tile + i;
-        v = (t >= W.wlo && t <= W.whi) ? v : -INFINITY;
+        v = (t >= lo && t <= hi) ? v : -INFINITY;
         x[4 * tile + i] = v;
         mx = fmaxf(mx, v);
       }
@@ -640,6 +656,8 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
 
       m_run = -INFINITY;
       d_run = 0.0f;
+      col_hi = cu.qpos + col_tok;
+      col_lo = a.window_left < 0 ? 0 : col_hi - a.window_left;
 #pragma unroll
       for (int b = 0; b < G_::kPvMfma; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
       const int base = cu.tb & ~(kStepTokens - 1);
@@ -751,8 +769,8 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
         s_pages[buf ^ 1][i] = npidx[Wn.wpage0 + i];
       if (threadIdx.x == 0) s_ticket[par] = nxt < a.num_items ? 2 * (int)gridDim.x + (int)tk : a.num_items;
       d_run = wave_sum_over_groups(d_run);
-      float* sacc = reinterpret_cast<float*>(vl);   // [16 heads][HD], own region
-      if (n < group) {
+      float* sacc = reinterpret_cast<float*>(vl);   // [16 rows][HD], own region
+      if (n < cols) {
 #pragma unroll
         for (int b = 0; b < G_::kPvMfma; ++b)
 #pragma unroll
@@ -770,8 +788,9 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
       // ---- merge the wavefronts' states, in wavefront order: one float4
       // column of one head per thread
       constexpr int cols4 = HD / 4;
-      for (int e = threadIdx.x; !drop && e < group * cols4; e += kWaves * 64) {
+      for (int e = threadIdx.x; !drop && e < cols * cols4; e += kWaves * 64) {
         const int h = e / cols4, c = 4 * (e - h * cols4);
+        const int qj = h / group, gh = h - qj * group;   // query token, head of row h
         float M = s_m[0][h];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][h]);
@@ -784,18 +803,22 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
           num += sw * *reinterpret_cast<const f32x4*>(smem + w * G_::kWaveLds + (h * HD + c) * 4);
           den += sw * s_d[w][h];
         }
+        // (a row with no visible token in this unit, possible only for an
+        // early query token of a split request, is an empty state)
         f32x4 ov;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = num[i] / den * a.v_scale;
-        const float lse2 = M + __builtin_amdgcn_logf(den);
-        const int qh = qh0 + h;
+        for (int i = 0; i < 4; ++i) ov[i] = den > 0.0f ? num[i] / den * a.v_scale : 0.0f;
+        const float lse2 = den > 0.0f ? M + __builtin_amdgcn_logf(den) : -INFINITY;
+        const int qh = qh0 + gh;
         if (cu.partial < 0) {
-          store_out4(a.o, ((size_t)cu.request * a.num_qo_heads + qh) * HD + c, ov, a.o_bf16);
-          if (a.lse != nullptr && c == 0) a.lse[(size_t)cu.request * a.num_qo_heads + qh] = lse2 * kLn2;
+          const size_t orow = ((size_t)cu.request * a.q_len + qj) * a.num_qo_heads + qh;
+          store_out4(a.o, orow * HD + c, ov, a.o_bf16);
+          if (a.lse != nullptr && c == 0) a.lse[orow] = lse2 * kLn2;
         } else {
           // device-coherent stores: the merging workgroup may sit on another XCD
-          store_coherent4(ws_o_rsrc, (uint32_t)(((size_t)cu.partial * a.num_qo_heads + qh) * HD + c) * 4, ov);
-          if (c == 0) store_coherent(a.ws_lse + (size_t)cu.partial * a.num_qo_heads + qh, lse2);
+          const size_t wrow = ((size_t)cu.partial * a.q_len + qj) * a.num_qo_heads + qh;
+          store_coherent4(ws_o_rsrc, (uint32_t)(wrow * HD + c) * 4, ov);
+          if (c == 0) store_coherent(a.ws_lse + wrow, lse2);
         }
       }
       if (!drop && cu.partial >= 0) {

@@ -16,7 +16,7 @@ namespace pkd {
 // on one work item; each wavefront takes kStepTokens tokens per step.
 constexpr int kWaves = 4;
 constexpr int kStepTokens = 32;
-constexpr int kMaxGroup = 16;       // q heads per kv head (one MFMA tile)
+constexpr int kMaxGroup = 16;       // query rows per kv head: G * Q (one MFMA tile)
 constexpr int kMergeRowsPerBlock = 4;
 // Units of a split request are merged in two levels: each run of
 // kMergeGroup consecutive units of a (request, kv head) first, then the runs.
@@ -72,6 +72,11 @@ struct HostPlan {
   std::vector<MergeRow> merges;
 };
 
+// Query tokens per request of a plan (0 in the parameters means 1).
+inline int32_t q_len_of(const pkd_plan_params& p) {
+  return p.q_len_per_req > 1 ? p.q_len_per_req : 1;
+}
+
 // Records `msg` as this thread's last error and returns `st`.
 pkd_status fail(pkd_status st, const std::string& msg);
 void clear_error();
@@ -116,15 +121,18 @@ struct DecodeArgs {
   const pkd_work_item* items;
   void* o;
   float* lse;
-  float* ws_o;          // [num_partials][num_qo_heads][head_dim]
+  float* ws_o;          // [num_partials][q_len][num_qo_heads][head_dim]
   size_t ws_o_bytes;
-  float* ws_lse;        // [num_partials][num_qo_heads], base-2
+  float* ws_lse;        // [num_partials][q_len][num_qo_heads], base-2
   int64_t page_stride;  // elements between pages
   int32_t slot_stride;  // elements between tokens of a page
   int32_t head_stride;  // elements between kv heads of a page
   int32_t num_qo_heads;
   int32_t num_kv_heads;
   int32_t group;        // G
+  int32_t q_len;        // Q, query tokens per request
+  int32_t cols;         // G * Q <= kMaxGroup: query rows of a unit
+  int32_t window_left;  // -1, or the left window of each query token
   int32_t log2_page;
   int32_t o_bf16;       // output dtype: 0 = f16, 1 = bf16
   float logit_scale;    // sm_scale*q_scale*k_scale (times log2 e if no cap)

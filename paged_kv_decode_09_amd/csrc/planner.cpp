@@ -89,6 +89,12 @@ pkd_status check_params(const pkd_plan_params& p) {
     return fail(PKD_EUNSUPPORTED,
                 fmt("group size %d (num_qo_heads/num_kv_heads) exceeds %d",
                     group, kMaxGroup));
+  if (p.q_len_per_req < 0)
+    return fail(PKD_EINVAL, fmt("q_len_per_req %d < 0", p.q_len_per_req));
+  if ((int64_t)group * q_len_of(p) > kMaxGroup)
+    return fail(PKD_EUNSUPPORTED,
+                fmt("group size %d x q_len_per_req %d exceeds %d query rows per kv head",
+                    group, q_len_of(p), kMaxGroup));
   if (p.head_dim != 64 && p.head_dim != 128 && p.head_dim != 256)
     return fail(PKD_EUNSUPPORTED,
                 fmt("head_dim %d not in {64, 128, 256}", p.head_dim));
@@ -144,6 +150,7 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
     return fail(PKD_EINVAL, fmt("indptr[0] = %d, must be 0", indptr[0]));
 
   const int32_t P = p.page_size;
+  const int32_t Q = q_len_of(p);
   std::vector<Req> reqs(B);
   int64_t attended = 0;
   int32_t max_pages = 0;
@@ -163,9 +170,14 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
       return fail(PKD_EUNSUPPORTED,
                   fmt("request %d has kv_len %lld > %d", i, (long long)L,
                       INT32_MAX / 2));
+    if (L < Q)
+      return fail(PKD_EINVAL, fmt("request %d has kv_len %lld < q_len_per_req %d: its "
+                                  "first query token would have no position",
+                                  i, (long long)L, Q));
     Req r;
     r.kv_len = (int32_t)L;
-    r.start = p.window_left < 0 ? 0 : std::max<int32_t>(0, r.kv_len - 1 - p.window_left);
+    // the first query token (position L-Q) has the earliest window start
+    r.start = p.window_left < 0 ? 0 : std::max<int32_t>(0, r.kv_len - Q - p.window_left);
     r.pages = (int32_t)np;
     reqs[i] = r;
     attended += r.kv_len - r.start;
@@ -257,6 +269,7 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
         u.it.partial = split_req ? partials + (int32_t)c : -1;
         u.it.chunk = (int32_t)c;
         u.it.num_chunks = (int32_t)n;
+        u.it.query_pos = r.kv_len - Q;
         u.tokens = ranges[c].second - ranges[c].first;
         units.push_back(u);
       }
@@ -294,10 +307,10 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
       INT32_MAX / 2)
     return fail(PKD_EUNSUPPORTED, "too many split requests for the merge counters");
   // the merge addresses one request's partial states with 32-bit offsets
-  if ((int64_t)partials * p.num_qo_heads * p.head_dim * 4 > INT32_MAX)
-    return fail(PKD_EUNSUPPORTED, fmt("%d partial states of %d heads x %d exceed the "
+  if ((int64_t)partials * Q * p.num_qo_heads * p.head_dim * 4 > INT32_MAX)
+    return fail(PKD_EUNSUPPORTED, fmt("%d partial states of %d query rows x %d exceed the "
                                       "2 GiB workspace limit",
-                                      partials, p.num_qo_heads, p.head_dim));
+                                      partials, Q * p.num_qo_heads, p.head_dim));
   pkd_plan_info& info = out->info;
   info.num_items = (int32_t)out->items.size();
   info.num_workgroups = (int32_t)nwg;
@@ -309,8 +322,8 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
   info.workspace_bytes =
       partials == 0
           ? 0
-          : workspace_lse_offset(partials, p.num_qo_heads, p.head_dim) +
-                (size_t)partials * p.num_qo_heads * 4;
+          : workspace_lse_offset(partials, Q * p.num_qo_heads, p.head_dim) +
+                (size_t)partials * Q * p.num_qo_heads * 4;
   clear_error();
   return PKD_OK;
 }

@@ -7,7 +7,9 @@ tests and the CPU oracle's tests take their inputs from here.
 Named workloads follow the shapes of the class example on the "FlashInfer
 attention kernels" page (flashinfer.decode › BatchDecodeWithPagedKVCacheWrapper)
 and four decode workloads of the same kind (a serving batch, long-context
-split-KV, a Gemma-2-style soft-capped windowed decode, and fp8 KV).
+split-KV, a Gemma-2-style soft-capped windowed decode, and fp8 KV), plus the
+serving batch with several query tokens per request (run()'s
+q_len_per_req).
 
 Recipe (per workload, ``rng = numpy.random.default_rng(seed)``, drawn in this
 order): lengths -> page permutation -> q -> K/V pool. The pool is drawn with a
@@ -49,6 +51,7 @@ class Workload:
     fixed_split_size: int = 0
     k_scale: float = 1.0
     v_scale: float = 1.0
+    q_len_per_req: int = 1    # query tokens per request (q has batch * this rows)
     note: str = field(default="", compare=False)
 
     @property
@@ -80,6 +83,11 @@ WORKLOADS = {
         "fp8_kv", 5, 128, 64, 8, 128, 16, "bf16", "e4m3", "bf16", "NHD",
         ("uniform", 2048, 16384), pages="perm_used", k_scale=1.0 / 64,
         v_scale=1.0 / 64, note="E4M3 KV with per-tensor scale 1/64"),
+    "spec_decode": Workload(
+        "spec_decode", 6, 64, 32, 8, 128, 16, "bf16", "bf16", "bf16", "HND",
+        ("uniform", 512, 4096), pages="perm_pool", pool_pages=20000,
+        q_len_per_req=4,
+        note="the serving batch with 4 query tokens per request (causal)"),
 }
 
 
@@ -147,8 +155,8 @@ def make_page_table(w: Workload, rng: np.random.Generator) -> PageTable:
 
 def make_q(w: Workload, rng: np.random.Generator, scale: float = 1.0,
            device="cpu") -> torch.Tensor:
-    x = rng.standard_normal((w.batch, w.num_qo_heads, w.head_dim),
-                            dtype=np.float32) * np.float32(scale)
+    x = rng.standard_normal((w.batch * w.q_len_per_req, w.num_qo_heads,
+                             w.head_dim), dtype=np.float32) * np.float32(scale)
     return torch.from_numpy(x).to(TORCH_DTYPES[w.q_dtype]).to(device)
 
 

@@ -21,7 +21,8 @@ def plan_for(w, case, **overrides):
               logits_soft_cap=w.logits_soft_cap or None,
               q_data_type=w.q_dtype, kv_data_type=w.kv_dtype,
               o_data_type=w.o_dtype, sm_scale=w.sm_scale,
-              fixed_split_size=w.fixed_split_size or None)
+              fixed_split_size=w.fixed_split_size or None,
+              q_len_per_req=w.q_len_per_req)
     kw.update(overrides)
     indices = torch.from_numpy(case.pt.indices).to("cuda")
     return pkd.PagedDecodePlan(case.pt.indptr, indices, case.pt.last_page_len,
@@ -55,17 +56,28 @@ def sub_pool(case, requests):
         np.array(last, np.int32)
 
 
+def rows_of(w, requests):
+    """Rows of q / o / lse that hold the given requests' query tokens."""
+    Q = w.q_len_per_req
+    return [i * Q + j for i in requests for j in range(Q)]
+
+
 def oracle_for(w, case, requests=None, split_pages=None, q=None):
-    """fp64 oracle o [len(requests), nq, hd] and lse for the case's inputs."""
+    """fp64 oracle o [len(requests) * Q, nq, hd] and lse for the case's
+    inputs (Q query tokens per request)."""
     reqs = list(range(w.batch)) if requests is None else list(requests)
     pool, indptr, indices, last = sub_pool(case, reqs)
-    qq = (case.q if q is None else q)[torch.tensor(reqs)]
+    qq = (case.q if q is None else q)[torch.tensor(rows_of(w, reqs))]
     qn = wl.raw_numpy(qq, w.q_dtype)
     pn = wl.raw_numpy(pool, w.kv_dtype)
     args = (qn, pn, w.layout, indptr, indices, last, w.page_size, w.q_dtype,
             w.kv_dtype, w.sm_scale)
     kw = dict(logits_soft_cap=w.logits_soft_cap, window_left=w.window_left,
               k_scale=w.k_scale, v_scale=w.v_scale)
+    if w.q_len_per_req > 1:
+        return oracle.batch_decode_multi(qn, pn, w.layout, indptr, indices, last,
+                                         w.page_size, w.q_len_per_req, w.q_dtype,
+                                         w.kv_dtype, w.sm_scale, **kw)
     if split_pages:
         return oracle.batch_decode_split(*args, split_pages, **kw)
     return oracle.batch_decode(*args, **kw)

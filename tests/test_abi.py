@@ -26,12 +26,12 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == 8
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.pkd_abi_version() == pkd.ABI_VERSION == 2
+    assert lib.pkd_abi_version() == pkd.ABI_VERSION == 3
 
 
 def test_struct_sizes_match_header():
-    assert ctypes.sizeof(pkd.pkd_plan_params) == 14 * 4
-    assert ctypes.sizeof(pkd.pkd_work_item) == 32
+    assert ctypes.sizeof(pkd.pkd_plan_params) == 15 * 4
+    assert ctypes.sizeof(pkd.pkd_work_item) == 36
     assert ctypes.sizeof(pkd.pkd_plan_info) == 40
 
 
@@ -58,6 +58,9 @@ def query(indptr, last, num_cus=256, **kw):
     (dict(q_data_type="float8_e4m3fn"), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "q_dtype"),
     (dict(q_data_type="float16", kv_data_type="bfloat16"), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "kv_dtype"),
     (dict(o_data_type="float8_e4m3fn"), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "o_dtype"),
+    (dict(q_len_per_req=-1), [0, 1], [1], pkd.PKD_EINVAL, "q_len_per_req -1"),
+    (dict(q_len_per_req=5), [0, 1], [8], pkd.PKD_EUNSUPPORTED, "group size 4 x q_len_per_req 5"),
+    (dict(q_len_per_req=3), [0, 1, 2], [9, 2], pkd.PKD_EINVAL, "request 1 has kv_len 2 < q_len_per_req 3"),
     (dict(sm_scale=float("inf")), [0, 1], [1], pkd.PKD_EINVAL, "sm_scale"),
 ])
 def test_plan_rejects_invalid_input(kw, indptr, last, status, needle):
@@ -245,3 +248,35 @@ def test_auto_split_respects_minimum_unit():
 def test_empty_batch_plans_nothing():
     info, items = query([0], [])
     assert info.num_items == 0 and items == [] and info.workspace_bytes == 0
+
+
+@pytest.mark.parametrize("window", [-1, 0, 7, 100])
+@pytest.mark.parametrize("split", [0, 1, 3])
+@pytest.mark.parametrize("Q", [1, 2, 4])
+def test_multi_token_units_cover_the_first_tokens_window(Q, split, window):
+    rng = np.random.default_rng(Q * 31 + split)
+    lens = np.concatenate([[Q, Q + 1, 16 * 3], rng.integers(Q, 2000, 9)])
+    pages = (lens + 15) // 16
+    indptr = np.concatenate([[0], np.cumsum(pages)]).astype(np.int32)
+    last = (lens - 16 * (pages - 1)).astype(np.int32)
+    info, items = query(indptr, last, q_len_per_req=Q,
+                        fixed_split_size=split or None, window_left=window)
+    # the union of the query tokens' windows starts at the first token's
+    starts = [0 if window < 0 else max(0, int(L) - Q - window) for L in lens]
+    coverage(items, 2, lens, starts)
+    for it in items:
+        assert it.query_pos == lens[it.request] - Q
+    # workspace: Q query rows of every q head per partial state
+    if info.num_partials:
+        rows = info.num_partials * Q * 8
+        assert info.workspace_bytes >= rows * 128 * 4 + rows * 4
+
+
+def test_multi_token_default_is_one_token():
+    a, ia = query([0, 3], [5])
+    b, ib = query([0, 3], [5], q_len_per_req=1)
+    c, ic = query([0, 3], [5], q_len_per_req=0)
+    assert [(i.token_begin, i.token_end, i.query_pos) for i in ia] == \
+        [(i.token_begin, i.token_end, i.query_pos) for i in ib] == \
+        [(i.token_begin, i.token_end, i.query_pos) for i in ic]
+    assert ia[0].query_pos == 16 * 2 + 5 - 1

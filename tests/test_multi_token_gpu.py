@@ -1,0 +1,155 @@
+"""GPU parity of decode with several query tokens per request (run()'s
+q_len_per_req) against the fp64 oracle, through the C-ABI.
+
+Query token j of a request sits at position kv_len - Q + j (the causal
+diagonal of the prefill mask example) and attends the tokens up to it. Every
+test prints its case before it touches the GPU."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_decode_09_amd as pkd
+from paged_kv_decode_09_amd import workloads as wl
+from helpers import (LSE_TOL, max_abs, o_tol, oracle_for, plan_for, rows_of,
+                     run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def check(w, case, o, lse, requests=None):
+    ref_o, ref_l = oracle_for(w, case, requests)
+    idx = slice(None) if requests is None else torch.tensor(rows_of(w, requests))
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    eo, el = max_abs(o[idx], ref_o), max_abs(lse[idx], ref_l)
+    assert eo <= o_tol(w), f"o max-abs {eo} > {o_tol(w)}"
+    assert el <= LSE_TOL, f"lse max-abs {el} > {LSE_TOL}"
+    return eo, el
+
+
+# (head_dim, group, Q, layout, dtype, page_size): G * Q <= 16 query rows
+GRID = [
+    (128, 4, 4, "HND", "bf16", 16),
+    (128, 8, 2, "NHD", "f16", 16),
+    (128, 1, 16, "NHD", "bf16", 4),
+    (64, 2, 8, "HND", "f16", 1),
+    (64, 4, 3, "NHD", "bf16", 16),
+    (256, 2, 4, "NHD", "bf16", 16),
+    (256, 1, 5, "HND", "f16", 2),
+    (128, 2, 7, "NHD", "f16", 64),
+]
+
+
+@pytest.mark.parametrize("cfg", GRID, ids=lambda c: "hd{}-g{}-q{}-{}-{}-p{}".format(*c))
+@pytest.mark.parametrize("split", [None, 1, 3])
+def test_multi_token_grid(cfg, split):
+    hd, group, Q, layout, dt, ps = cfg
+    w = wl.small_workload(seed=41, batch=6, num_qo_heads=2 * group, num_kv_heads=2,
+                          head_dim=hd, layout=layout, q_dtype=dt, kv_dtype=dt,
+                          o_dtype=dt, page_size=ps, q_len_per_req=Q,
+                          lengths=("fixed", [Q, Q + 1, 17, 100, 333, 64 + Q]))
+    say(w, "split", split)
+    case = wl.make_case(w, device="cuda")
+    o, lse, _ = run_gpu(w, case, fixed_split_size=split)
+    assert tuple(o.shape) == (6 * Q, 2 * group, hd)
+    check(w, case, o, lse)
+
+
+@pytest.mark.parametrize("cap,window", [(0.0, 0), (0.0, 3), (30.0, 40), (50.0, -1)])
+def test_multi_token_window_and_cap(cap, window):
+    w = wl.small_workload(seed=43, batch=5, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                          q_dtype="bf16", kv_dtype="bf16", o_dtype="bf16",
+                          q_len_per_req=4, logits_soft_cap=cap, window_left=window,
+                          lengths=("fixed", [4, 9, 70, 600, 1500]))
+    say(w)
+    case = wl.make_case(w, device="cuda", q_scale=8.0 if cap else 1.0)
+    for split in (None, 1, 2):
+        o, lse, _ = run_gpu(w, case, fixed_split_size=split)
+        check(w, case, o, lse)
+
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_multi_token_fp8_kv(layout):
+    w = wl.small_workload(seed=47, batch=4, num_qo_heads=16, num_kv_heads=2, head_dim=128,
+                          q_dtype="bf16", kv_dtype="e4m3", o_dtype="bf16", layout=layout,
+                          q_len_per_req=2, k_scale=1.0 / 64, v_scale=1.0 / 64,
+                          lengths=("fixed", [2, 41, 513, 2000]))
+    say(w)
+    case = wl.make_case(w, device="cuda")
+    for split in (None, 4):
+        o, lse, _ = run_gpu(w, case, fixed_split_size=split)
+        check(w, case, o, lse)
+
+
+@pytest.mark.parametrize("split", [None, 2])
+def test_last_query_token_equals_one_token_decode_bitwise(split):
+    """Without a window, the last query token's column sees exactly what a
+    one-token decode of the same request sees, through the same units: its
+    arithmetic does not depend on the other columns, so the bits agree."""
+    w = wl.small_workload(seed=53, batch=5, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                          q_dtype="f16", kv_dtype="f16", o_dtype="f16", q_len_per_req=4,
+                          lengths=("fixed", [4, 50, 700, 1300, 2600]))
+    say(w, "split", split)
+    case = wl.make_case(w, device="cuda")
+    o, lse, _ = run_gpu(w, case, fixed_split_size=split)
+    w1 = replace(w, q_len_per_req=1)
+    q1 = case.q[3::4].contiguous()
+    o1, l1, _ = run_gpu(w1, case, q=q1, fixed_split_size=split)
+    assert torch.equal(o[3::4], o1) and torch.equal(lse[3::4], l1)
+
+
+def test_multi_token_poisoned_slots_do_not_leak():
+    w = wl.small_workload(seed=59, batch=6, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                          q_len_per_req=3, lengths=("uniform", 3, 900), pool_pages=400,
+                          pages="perm_pool")
+    say(w)
+    clean = wl.make_case(w, device="cuda")
+    dirty = wl.make_case(w, device="cuda", poison=True)
+    for split in (None, 2):
+        o1, l1, _ = run_gpu(w, clean, fixed_split_size=split)
+        o2, l2, _ = run_gpu(w, dirty, fixed_split_size=split)
+        assert not torch.isnan(o2).any() and not torch.isnan(l2).any()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_multi_token_rejects_mismatched_shapes():
+    w = wl.small_workload(seed=61, batch=2, q_len_per_req=2, lengths=("fixed", [5, 9]))
+    say(w)
+    case = wl.make_case(w, device="cuda")
+    plan = plan_for(w, case)
+    with pytest.raises(pkd.PkdError):
+        plan.run(case.q[:2].contiguous(), case.pool)   # one row per request: wrong
+    wrapper = pkd.BatchDecodeWithPagedKVCacheWrapper(
+        torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
+    wrapper.plan(case.pt.indptr, torch.from_numpy(case.pt.indices).cuda(),
+                 case.pt.last_page_len, 8, 2, 64, 16, q_len_per_req=2)
+    with pytest.raises(pkd.PkdError):
+        wrapper.run(case.q, case.pool, q_len_per_req=3)
+    o = wrapper.run(case.q, case.pool, q_len_per_req=2)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (4, 8, 64)
+
+
+def test_spec_decode_full_size():
+    """The serving batch with 4 query tokens per request, at full size, on
+    sampled requests; and q = 0 pins each token's attended count."""
+    w = wl.WORKLOADS["spec_decode"]
+    say(w.name)
+    case = wl.make_case(w, device="cuda")
+    o, lse, plan = run_gpu(w, case)
+    L = case.pt.lengths
+    reqs = sorted({0, w.batch - 1, int(np.argmin(L)), int(np.argmax(L)), 17})
+    eo, el = check(w, case, o, lse, reqs)
+    say(w.name, "requests", reqs, "o max-abs", eo, "lse max-abs", el,
+        "items", plan.info.num_items)
+    _, l0 = plan.run(torch.zeros_like(case.q), case.pool, return_lse=True)
+    torch.cuda.synchronize()
+    Q = w.q_len_per_req
+    n = np.array([[int(Li) - Q + j + 1 for j in range(Q)] for Li in L]).reshape(-1)
+    err = np.abs(l0.double().cpu().numpy() - np.log(n)[:, None])
+    assert np.all(err < np.minimum(2e-5, 0.45 / n)[:, None]), float(np.max(err))
