@@ -106,7 +106,7 @@ typedef struct {
   int32_t kv_head;
   int32_t token_begin;      /* first attended token of the chunk            */
   int32_t token_end;        /* one past the last attended token             */
-  int32_t page_base;        /* indptr[request]                              */
+  int32_t page_base;        /* indptr[request] (block table: request*row)   */
   int32_t partial;          /* -1: writes o/lse; else its workspace slot    */
   int32_t chunk;            /* unit index within the request (ascending)    */
   int32_t num_chunks;       /* units of the request per kv head (1: unsplit) */
@@ -160,6 +160,31 @@ pkd_status pkd_plan_query(const pkd_plan_params* params, const int32_t* indptr,
                           const int32_t* last_page_len, int32_t num_cus,
                           pkd_plan_info* info, pkd_work_item* items,
                           int32_t capacity);
+
+/* plan() from a block table instead of the CSR page table: the page_table /
+ * seq_lens input of the XQA decode on the same page ("page_table" [batch,
+ * nb_pages_per_seq] int32, K and V sharing it; "seq_lens" per request), also
+ * the seq_lens / block_tables parameters of the trtllm-gen prefill plan().
+ *   seq_lens       host, int32 [B], L_i >= 1 (>= Q), read during the call only
+ *   block_tables   DEVICE, int32 [B][max_blocks_per_seq], row-major,
+ *                  BORROWED like indices: request i owns pages
+ *                  block_tables[i][0 .. ceil(L_i/P)); later entries of the
+ *                  row are never read
+ * Equivalent to pkd_plan_create with indptr[i+1]-indptr[i] = ceil(L_i/P),
+ * last_page_len[i] = L_i - P*(ceil(L_i/P)-1) and the index array read at
+ * row i of the table; runs of such a plan give the same bits as that plan.
+ * Errors as pkd_plan_create, and PKD_EINVAL when max_blocks_per_seq < 1 or
+ * a request needs more pages than a row holds. */
+pkd_status pkd_plan_create_block_table(const pkd_plan_params* params, const int32_t* seq_lens,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       void* stream, pkd_plan** out);
+
+/* Host-only planning of a block-table batch (as pkd_plan_query). The
+ * items' page_base is i * max_blocks_per_seq. */
+pkd_status pkd_plan_query_block_table(const pkd_plan_params* params, const int32_t* seq_lens,
+                                      int32_t max_blocks_per_seq, int32_t num_cus,
+                                      pkd_plan_info* info, pkd_work_item* items,
+                                      int32_t capacity);
 
 pkd_status pkd_plan_get_info(const pkd_plan* plan, pkd_plan_info* info);
 

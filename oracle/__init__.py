@@ -9,6 +9,7 @@ from .fp8 import E4M3_TABLE, e4m3_to_f64
 from .oracle import (
     widen,
     kv_lengths,
+    csr_from_block_table,
     window_start,
     gather_request,
     attention_state,
@@ -26,6 +27,7 @@ __all__ = [
     "e4m3_to_f64",
     "widen",
     "kv_lengths",
+    "csr_from_block_table",
     "window_start",
     "gather_request",
     "attention_state",

@@ -91,6 +91,28 @@ def kv_lengths(indptr, last_page_len, page_size: int) -> np.ndarray:
     return page_size * (npages - 1) + last
 
 
+def csr_from_block_table(seq_lens, block_tables, page_size: int):
+    """CSR page table (indptr, indices, last_page_len) of a block table.
+
+    The XQA decode on the API page takes page_table [batch, nb_pages_per_seq]
+    (K and V share it) and seq_lens; request i owns the pages
+    block_tables[i, 0 : ceil(seq_lens[i] / page_size)], and its last page
+    holds seq_lens[i] - page_size * (pages - 1) tokens.
+    """
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    block_tables = np.asarray(block_tables)
+    if np.any(seq_lens < 1):
+        raise ValueError("every request needs at least one token")
+    npages = (seq_lens + page_size - 1) // page_size
+    if np.any(npages > block_tables.shape[1]):
+        raise ValueError("a request needs more pages than its row holds")
+    indptr = np.concatenate([[0], np.cumsum(npages)]).astype(np.int32)
+    indices = np.concatenate([block_tables[i, :n] for i, n in
+                              enumerate(npages)]).astype(np.int32)
+    last = (seq_lens - page_size * (npages - 1)).astype(np.int32)
+    return indptr, indices, last
+
+
 def window_start(kv_len: int, window_left: int) -> int:
     """First attended token of a request whose query sits at kv_len-1."""
     if window_left < 0:

@@ -77,6 +77,13 @@ _SIGS = {
                                       ctypes.c_int32,
                                       ctypes.POINTER(pkd_plan_info), _P,
                                       ctypes.c_int32]),
+    "pkd_plan_create_block_table": (ctypes.c_int, [ctypes.POINTER(pkd_plan_params),
+                                                   _P, _P, ctypes.c_int32, _P,
+                                                   ctypes.POINTER(_P)]),
+    "pkd_plan_query_block_table": (ctypes.c_int, [ctypes.POINTER(pkd_plan_params), _P,
+                                                  ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.POINTER(pkd_plan_info), _P,
+                                                  ctypes.c_int32]),
     "pkd_plan_get_info": (ctypes.c_int, [_P, ctypes.POINTER(pkd_plan_info)]),
     "pkd_plan_destroy": (None, [_P]),
     "pkd_run": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_float,
@@ -188,6 +195,23 @@ def plan_query(indptr, last_page_len, num_cus: int = 256, **kw):
     return info, list(items)[:info.num_items]
 
 
+def plan_query_block_table(seq_lens, max_blocks_per_seq: int,
+                           num_cus: int = 256, **kw):
+    """Host-only planning of a block-table batch: (pkd_plan_info, items)."""
+    sl = _host_i32(seq_lens)
+    params = make_params(len(sl), **kw)
+    info = pkd_plan_info()
+    _check(lib().pkd_plan_query_block_table(ctypes.byref(params), sl.ctypes.data,
+                                            int(max_blocks_per_seq), num_cus,
+                                            ctypes.byref(info), None, 0))
+    items = (pkd_work_item * max(info.num_items, 1))()
+    _check(lib().pkd_plan_query_block_table(ctypes.byref(params), sl.ctypes.data,
+                                            int(max_blocks_per_seq), num_cus,
+                                            ctypes.byref(info),
+                                            ctypes.cast(items, _P), info.num_items))
+    return info, list(items)[:info.num_items]
+
+
 def _split_cache(paged_kv_cache, layout: int, page_size: int,
                  num_kv_heads: int, head_dim: int):
     """(k pointer, v pointer, page stride in elements, dtype) of a cache."""
@@ -219,9 +243,15 @@ def _split_cache(paged_kv_cache, layout: int, page_size: int,
 
 
 class PagedDecodePlan:
-    """One plan (pkd_plan_create): a batch's page table, reused across runs."""
+    """One plan (pkd_plan_create): a batch's page table, reused across runs.
 
-    def __init__(self, indptr, indices: torch.Tensor, last_page_len,
+    The page table is either CSR (indptr, indices, last_page_len) or, with
+    ``block_tables`` (int32 device [B, max_blocks]) and ``seq_lens`` (host or
+    device int32 [B]), a block table (pkd_plan_create_block_table); then
+    indptr / indices / last_page_len are None.
+    """
+
+    def __init__(self, indptr, indices: Optional[torch.Tensor], last_page_len,
                  num_qo_heads: int, num_kv_heads: int, head_dim: int,
                  page_size: int, kv_layout: str = "NHD", window_left: int = -1,
                  logits_soft_cap: Optional[float] = None,
@@ -229,21 +259,46 @@ class PagedDecodePlan:
                  o_data_type=None, sm_scale: Optional[float] = None,
                  fixed_split_size: Optional[int] = None,
                  disable_split_kv: bool = False, stream=None,
-                 q_len_per_req: int = 1):
+                 q_len_per_req: int = 1, seq_lens=None,
+                 block_tables: Optional[torch.Tensor] = None):
         self._handle = None
-        ip, lp = _host_i32(indptr), _host_i32(last_page_len)
-        if indices.dtype != torch.int32 or not indices.is_cuda:
-            raise PkdError(PKD_EINVAL, "indices must be an int32 device tensor")
-        self.params = make_params(len(lp), num_qo_heads, num_kv_heads, head_dim,
+        table = block_tables if block_tables is not None else indices
+        if table is None or table.dtype != torch.int32 or not table.is_cuda:
+            raise PkdError(PKD_EINVAL, "indices / block_tables must be an int32 "
+                           "device tensor")
+        if block_tables is not None:
+            if indptr is not None or indices is not None or \
+                    last_page_len is not None or seq_lens is None:
+                raise PkdError(PKD_EINVAL, "give either indptr/indices/"
+                               "last_page_len or block_tables/seq_lens")
+            if block_tables.dim() != 2:
+                raise PkdError(PKD_EINVAL, "block_tables must be [batch, "
+                               "max_blocks]")
+            sl = _host_i32(seq_lens)
+            batch = len(sl)
+            if block_tables.shape[0] != batch:
+                raise PkdError(PKD_EINVAL, "block_tables and seq_lens differ "
+                               "in batch size")
+        else:
+            ip, lp = _host_i32(indptr), _host_i32(last_page_len)
+            batch = len(lp)
+        self.params = make_params(batch, num_qo_heads, num_kv_heads, head_dim,
                                   page_size, kv_layout, window_left,
                                   logits_soft_cap, q_data_type, kv_data_type,
                                   o_data_type, sm_scale, fixed_split_size,
                                   disable_split_kv, q_len_per_req)
-        self.indices = indices.contiguous()   # borrowed by the plan: keep alive
+        self.indices = table.contiguous()   # borrowed by the plan: keep alive
         h = _P()
-        _check(lib().pkd_plan_create(ctypes.byref(self.params), ip.ctypes.data,
-                                     lp.ctypes.data, self.indices.data_ptr(),
-                                     _stream_ptr(stream), ctypes.byref(h)))
+        if block_tables is not None:
+            _check(lib().pkd_plan_create_block_table(
+                ctypes.byref(self.params), sl.ctypes.data,
+                self.indices.data_ptr(), int(self.indices.shape[1]),
+                _stream_ptr(stream), ctypes.byref(h)))
+        else:
+            _check(lib().pkd_plan_create(ctypes.byref(self.params),
+                                         ip.ctypes.data, lp.ctypes.data,
+                                         self.indices.data_ptr(),
+                                         _stream_ptr(stream), ctypes.byref(h)))
         self._handle = h
         self.info = pkd_plan_info()
         _check(lib().pkd_plan_get_info(self._handle, ctypes.byref(self.info)))
@@ -331,7 +386,11 @@ class BatchDecodeWithPagedKVCacheWrapper:
              kv_data_type=None, o_data_type=None, data_type=None,
              sm_scale=None, rope_scale=None, rope_theta=None,
              non_blocking=True, fixed_split_size=None,
-             disable_split_kv=False, q_len_per_req=1) -> None:
+             disable_split_kv=False, q_len_per_req=1, seq_lens=None,
+             block_tables=None) -> None:
+        """plan() of the page. With ``block_tables`` [B, max_blocks] and
+        ``seq_lens`` [B] the page table is a block table; indptr, indices and
+        last_page_len are then None."""
         if pos_encoding_mode != "NONE":
             raise PkdError(PKD_EUNSUPPORTED,
                            f"pos_encoding_mode {pos_encoding_mode!r}")
@@ -339,10 +398,14 @@ class BatchDecodeWithPagedKVCacheWrapper:
             q_data_type = data_type
             kv_data_type = kv_data_type or data_type
         self._plan = PagedDecodePlan(
-            indptr, indices.to(torch.int32), last_page_len, num_qo_heads,
+            indptr, None if indices is None else indices.to(torch.int32),
+            last_page_len, num_qo_heads,
             num_kv_heads, head_dim, page_size, self._layout, window_left,
             logits_soft_cap, q_data_type, kv_data_type, o_data_type, sm_scale,
-            fixed_split_size, disable_split_kv, q_len_per_req=q_len_per_req)
+            fixed_split_size, disable_split_kv, q_len_per_req=q_len_per_req,
+            seq_lens=seq_lens,
+            block_tables=None if block_tables is None else
+            block_tables.to(torch.int32))
         need = self._plan.workspace_bytes
         if self._ws.numel() * self._ws.element_size() < need:
             self._ws = torch.empty(need, dtype=torch.uint8,
@@ -385,4 +448,5 @@ def merge_states(v: torch.Tensor, s: torch.Tensor, out_dtype=None,
 
 __all__ = ["lib", "PkdError", "PagedDecodePlan",
            "BatchDecodeWithPagedKVCacheWrapper", "merge_states", "plan_query",
+           "plan_query_block_table",
            "make_params", "pkd_plan_params", "pkd_plan_info", "pkd_work_item"]

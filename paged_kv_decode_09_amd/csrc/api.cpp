@@ -110,18 +110,20 @@ extern "C" {
 
 int32_t pkd_abi_version(void) { return PKD_ABI_VERSION; }
 
-pkd_status pkd_plan_query(const pkd_plan_params* params, const int32_t* indptr,
-                          const int32_t* last_page_len, int32_t num_cus,
-                          pkd_plan_info* info, pkd_work_item* items,
-                          int32_t capacity) {
-  if (params == nullptr || info == nullptr)
-    return pkd::fail(PKD_EINVAL, "params and info must not be NULL");
+}  // extern "C"
+
+namespace {
+
+pkd_status query_plan(const pkd_plan_params* params, const int32_t* indptr,
+                      const int32_t* last_page_len, const int32_t* page_base,
+                      int32_t num_cus, pkd_plan_info* info, pkd_work_item* items,
+                      int32_t capacity) {
   pkd::HostPlan h;
   pkd_status st = pkd::check_params(*params);
   if (st != PKD_OK) return st;
   if (num_cus < 1) return pkd::fail(PKD_EINVAL, "num_cus " + std::to_string(num_cus) + " < 1");
   st = pkd::build_host_plan(*params, indptr, last_page_len,
-                            num_cus * pkd::decode_wgs_per_cu_table(*params), &h);
+                            num_cus * pkd::decode_wgs_per_cu_table(*params), &h, page_base);
   if (st != PKD_OK) return st;
   *info = h.info;
   if (items != nullptr) {
@@ -131,12 +133,9 @@ pkd_status pkd_plan_query(const pkd_plan_params* params, const int32_t* indptr,
   return PKD_OK;
 }
 
-pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
-                           const int32_t* last_page_len, const int32_t* indices,
-                           void* stream, pkd_plan** out) {
-  if (out == nullptr) return pkd::fail(PKD_EINVAL, "out must not be NULL");
-  *out = nullptr;
-  if (params == nullptr) return pkd::fail(PKD_EINVAL, "params must not be NULL");
+pkd_status create_plan(const pkd_plan_params* params, const int32_t* indptr,
+                       const int32_t* last_page_len, const int32_t* page_base,
+                       const int32_t* indices, void* stream, pkd_plan** out) {
   pkd_status st = pkd::check_params(*params);
   if (st != PKD_OK) return st;
   if (params->batch_size > 0 && indices == nullptr)
@@ -154,7 +153,7 @@ pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
   if (per_cu < 1) return pkd::fail(PKD_EHIP, "occupancy query of the decode kernel failed");
   pkd_plan* p = new (std::nothrow) pkd_plan();
   if (p == nullptr) return pkd::fail(PKD_ENOMEM, "plan allocation failed");
-  st = pkd::build_host_plan(*params, indptr, last_page_len, cus * per_cu, &p->host);
+  st = pkd::build_host_plan(*params, indptr, last_page_len, cus * per_cu, &p->host, page_base);
   if (st == PKD_OK) p->host.info.workgroups_per_cu = per_cu;
   if (st != PKD_OK) {
     delete p;
@@ -196,6 +195,58 @@ pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
   *out = p;
   pkd::clear_error();
   return PKD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkd_status pkd_plan_query(const pkd_plan_params* params, const int32_t* indptr,
+                          const int32_t* last_page_len, int32_t num_cus,
+                          pkd_plan_info* info, pkd_work_item* items,
+                          int32_t capacity) {
+  if (params == nullptr || info == nullptr)
+    return pkd::fail(PKD_EINVAL, "params and info must not be NULL");
+  return query_plan(params, indptr, last_page_len, nullptr, num_cus, info, items, capacity);
+}
+
+pkd_status pkd_plan_query_block_table(const pkd_plan_params* params, const int32_t* seq_lens,
+                                      int32_t max_blocks_per_seq, int32_t num_cus,
+                                      pkd_plan_info* info, pkd_work_item* items,
+                                      int32_t capacity) {
+  if (params == nullptr || info == nullptr)
+    return pkd::fail(PKD_EINVAL, "params and info must not be NULL");
+  pkd_status st = pkd::check_params(*params);
+  if (st != PKD_OK) return st;
+  std::vector<int32_t> indptr, last, base;
+  st = pkd::block_table_csr(*params, seq_lens, max_blocks_per_seq, &indptr, &last, &base);
+  if (st != PKD_OK) return st;
+  return query_plan(params, indptr.data(), last.data(), base.data(), num_cus, info, items,
+                    capacity);
+}
+
+pkd_status pkd_plan_create(const pkd_plan_params* params, const int32_t* indptr,
+                           const int32_t* last_page_len, const int32_t* indices,
+                           void* stream, pkd_plan** out) {
+  if (out == nullptr) return pkd::fail(PKD_EINVAL, "out must not be NULL");
+  *out = nullptr;
+  if (params == nullptr) return pkd::fail(PKD_EINVAL, "params must not be NULL");
+  return create_plan(params, indptr, last_page_len, nullptr, indices, stream, out);
+}
+
+pkd_status pkd_plan_create_block_table(const pkd_plan_params* params, const int32_t* seq_lens,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       void* stream, pkd_plan** out) {
+  if (out == nullptr) return pkd::fail(PKD_EINVAL, "out must not be NULL");
+  *out = nullptr;
+  if (params == nullptr) return pkd::fail(PKD_EINVAL, "params must not be NULL");
+  pkd_status st = pkd::check_params(*params);
+  if (st != PKD_OK) return st;
+  std::vector<int32_t> indptr, last, base;
+  st = pkd::block_table_csr(*params, seq_lens, max_blocks_per_seq, &indptr, &last, &base);
+  if (st != PKD_OK) return st;
+  return create_plan(params, indptr.data(), last.data(), base.data(), block_tables, stream,
+                     out);
 }
 
 pkd_status pkd_plan_get_info(const pkd_plan* plan, pkd_plan_info* info) {

@@ -87,9 +87,18 @@ pkd_status check_params(const pkd_plan_params& p);
 // The planner: validates the page table, picks the chunk size, builds the
 // work units and spreads them over `num_slots` workgroups (the decode
 // workgroups that fit on the GPU at once). Pure host code.
+// `page_base` (may be NULL) gives each request's offset into the page index
+// array when it is not indptr[i] (a block table: i * max_blocks_per_seq).
 pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
                            const int32_t* last_page_len, int32_t num_slots,
-                           HostPlan* out);
+                           HostPlan* out, const int32_t* page_base = nullptr);
+
+// CSR page counts of a block-table batch: indptr [B+1] (running page counts),
+// last_page_len [B] and page_base [B] = i * max_blocks, from seq_lens [B].
+pkd_status block_table_csr(const pkd_plan_params& p, const int32_t* seq_lens,
+                           int32_t max_blocks, std::vector<int32_t>* indptr,
+                           std::vector<int32_t>* last_page_len,
+                           std::vector<int32_t>* page_base);
 
 // Decode workgroups per compute unit the kernel instance of `p` is built for.
 int32_t decode_wgs_per_cu_table(const pkd_plan_params& p);

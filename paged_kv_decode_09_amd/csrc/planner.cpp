@@ -137,9 +137,40 @@ size_t workspace_lse_offset(int32_t num_partials, int32_t num_qo_heads,
   return (o_bytes + 255) & ~(size_t)255;
 }
 
+pkd_status block_table_csr(const pkd_plan_params& p, const int32_t* seq_lens,
+                           int32_t max_blocks, std::vector<int32_t>* indptr,
+                           std::vector<int32_t>* last_page_len,
+                           std::vector<int32_t>* page_base) {
+  const int32_t B = p.batch_size;
+  if (B > 0 && seq_lens == nullptr) return fail(PKD_EINVAL, "seq_lens must not be NULL");
+  if (max_blocks < 1)
+    return fail(PKD_EINVAL, fmt("max_blocks_per_seq %d < 1", max_blocks));
+  if ((int64_t)B * max_blocks > INT32_MAX)
+    return fail(PKD_EUNSUPPORTED, fmt("block table of %d x %d entries exceeds 2^31",
+                                      B, max_blocks));
+  indptr->assign(B + 1, 0);
+  last_page_len->assign(B, 0);
+  page_base->assign(B, 0);
+  const int64_t P = p.page_size;
+  for (int32_t i = 0; i < B; ++i) {
+    const int64_t L = seq_lens[i];
+    if (L < 1) return fail(PKD_EINVAL, fmt("seq_lens[%d] = %lld < 1", i, (long long)L));
+    const int64_t np = (L + P - 1) / P;
+    if (np > max_blocks)
+      return fail(PKD_EINVAL, fmt("seq_lens[%d] = %lld needs %lld pages > max_blocks_per_seq %d",
+                                  i, (long long)L, (long long)np, max_blocks));
+    if ((*indptr)[i] + np > INT32_MAX)
+      return fail(PKD_EUNSUPPORTED, "more than 2^31 pages in the batch");
+    (*indptr)[i + 1] = (*indptr)[i] + (int32_t)np;
+    (*last_page_len)[i] = (int32_t)(L - P * (np - 1));
+    (*page_base)[i] = i * max_blocks;
+  }
+  return PKD_OK;
+}
+
 pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
                            const int32_t* last_page_len, int32_t num_slots,
-                           HostPlan* out) {
+                           HostPlan* out, const int32_t* page_base) {
   pkd_status st = check_params(p);
   if (st != PKD_OK) return st;
   const int32_t B = p.batch_size;
@@ -265,7 +296,7 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
         u.it.kv_head = h;
         u.it.token_begin = (int32_t)ranges[c].first;
         u.it.token_end = (int32_t)ranges[c].second;
-        u.it.page_base = indptr[i];
+        u.it.page_base = page_base != nullptr ? page_base[i] : indptr[i];
         u.it.partial = split_req ? partials + (int32_t)c : -1;
         u.it.chunk = (int32_t)c;
         u.it.num_chunks = (int32_t)n;

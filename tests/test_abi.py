@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     lib = pkd.lib()
     names = header_functions()
-    assert len(names) == 8
+    assert len(names) == 10
     for name in names:
         assert hasattr(lib, name), name
     assert lib.pkd_abi_version() == pkd.ABI_VERSION == 3
@@ -280,3 +280,38 @@ def test_multi_token_default_is_one_token():
         [(i.token_begin, i.token_end, i.query_pos) for i in ib] == \
         [(i.token_begin, i.token_end, i.query_pos) for i in ic]
     assert ia[0].query_pos == 16 * 2 + 5 - 1
+
+
+@pytest.mark.parametrize("split", [0, 2])
+@pytest.mark.parametrize("Q", [1, 3])
+def test_block_table_plan_equals_csr_plan(split, Q):
+    rng = np.random.default_rng(5 + split + Q)
+    max_blocks = 70
+    lens = np.concatenate([[Q, 16, 17], rng.integers(Q, 16 * max_blocks, 20)])
+    npages = (lens + 15) // 16
+    indptr = np.concatenate([[0], np.cumsum(npages)]).astype(np.int32)
+    last = (lens - 16 * (npages - 1)).astype(np.int32)
+    kw = dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+              q_len_per_req=Q, fixed_split_size=split or None)
+    ci, citems = pkd.plan_query(indptr, last, 256, **kw)
+    bi, bitems = pkd.plan_query_block_table(lens, max_blocks, 256, **kw)
+    assert ci.num_items == bi.num_items and ci.workspace_bytes == bi.workspace_bytes
+    for a, b in zip(citems, bitems):
+        assert (a.request, a.kv_head, a.token_begin, a.token_end, a.partial,
+                a.chunk, a.num_chunks, a.query_pos) == \
+            (b.request, b.kv_head, b.token_begin, b.token_end, b.partial,
+             b.chunk, b.num_chunks, b.query_pos)
+        assert a.page_base == indptr[a.request]
+        assert b.page_base == b.request * max_blocks
+
+
+@pytest.mark.parametrize("lens,max_blocks,needle", [
+    ([5, 0], 4, "seq_lens[1] = 0"),
+    ([5, 65], 4, "needs 5 pages > max_blocks_per_seq 4"),
+    ([5], 0, "max_blocks_per_seq 0"),
+])
+def test_block_table_errors(lens, max_blocks, needle):
+    with pytest.raises(pkd.PkdError) as e:
+        pkd.plan_query_block_table(lens, max_blocks, 256, num_qo_heads=8,
+                                   num_kv_heads=2, head_dim=128, page_size=16)
+    assert needle in str(e.value) and e.value.status == pkd.PKD_EINVAL

@@ -516,3 +516,45 @@ def test_multi_token_rejects_short_requests():
     with pytest.raises(ValueError):
         oracle.batch_decode_multi(np.zeros((3, 1, 4)), cache, "NHD", indptr,
                                   indices, last, 4, 3, "f64", "f64", 1.0)
+
+
+# ------------------------------------------------------ block-table page input
+
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_block_table_gather_returns_written_rows(layout):
+    """Independent writer: tokens written, one by one, into the slot
+    t % P of page block_tables[i][t // P]; the oracle's CSR view of the
+    table must gather them back bit-exactly."""
+    rng = np.random.default_rng(12)
+    P, nkv, hd, max_blocks = 4, 2, 3, 6
+    lens = [1, 4, 5, 23, 24]
+    pool = 40
+    cache = np.full((pool, 2) + ((P, nkv, hd) if layout == "NHD" else (nkv, P, hd)),
+                    np.nan)
+    table = rng.permutation(pool)[:len(lens) * max_blocks].reshape(len(lens),
+                                                                  max_blocks)
+    dense = []
+    for i, L in enumerate(lens):
+        K = rng.standard_normal((L, nkv, hd))
+        V = rng.standard_normal((L, nkv, hd))
+        for t in range(L):
+            pg, sl = table[i, t // P], t % P
+            for h in range(nkv):
+                if layout == "NHD":
+                    cache[pg, 0, sl, h], cache[pg, 1, sl, h] = K[t, h], V[t, h]
+                else:
+                    cache[pg, 0, h, sl], cache[pg, 1, h, sl] = K[t, h], V[t, h]
+        dense.append((K, V))
+    indptr, indices, last = oracle.csr_from_block_table(lens, table, P)
+    assert list(oracle.kv_lengths(indptr, last, P)) == lens
+    for i, L in enumerate(lens):
+        K, V = oracle.gather_request(cache[:, 0], cache[:, 1], layout, indices,
+                                     indptr, i, L, P)
+        assert np.array_equal(K, dense[i][0]) and np.array_equal(V, dense[i][1])
+
+
+def test_block_table_rejects_short_rows():
+    with pytest.raises(ValueError):
+        oracle.csr_from_block_table([9], np.zeros((1, 2), np.int32), 4)
+    with pytest.raises(ValueError):
+        oracle.csr_from_block_table([0], np.zeros((1, 2), np.int32), 4)
