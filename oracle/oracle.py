@@ -139,13 +139,20 @@ def gather_request(k_cache, v_cache, layout: str, indices, indptr, i: int,
 
 
 def attention_state(q, K, V, sm_scale: float, logits_soft_cap: float = 0.0,
-                    return_weights: bool = False):
+                    return_weights: bool = False, sinks=None):
     """Dense softmax attention of one query row per q head over n tokens.
 
     q: [num_qo_heads, head_dim]; K, V: [n, num_kv_heads, head_dim]; all fp64.
     Returns (o [num_qo_heads, head_dim], lse [num_qo_heads]) and, if asked,
     the weights p [num_qo_heads, n]. With n == 0 the state is empty:
     o = 0, lse = -inf.
+
+    ``sinks`` (optional, [num_qo_heads]): the attention-sink values of the
+    XQA decode on the API page ("sinks" [num_kv_heads, head_group_ratio]
+    float32, flattened in q-head order). Reading taken: sink s of a q head
+    is one more logit in that head's softmax, compared with the final
+    (scaled, capped) logits, that carries no value row: o = sum_t e^x_t v_t /
+    (sum_t e^x_t + e^s), and lse = ln(sum_t e^x_t + e^s).
     """
     q = np.asarray(q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
@@ -166,8 +173,12 @@ def attention_state(q, K, V, sm_scale: float, logits_soft_cap: float = 0.0,
         if logits_soft_cap > 0:
             x = logits_soft_cap * np.tanh(x / logits_soft_cap)
         m = x.max()
+        if sinks is not None:
+            m = max(m, float(sinks[hq]))
         p = np.exp(x - m)
         z = p.sum()
+        if sinks is not None:
+            z += math.exp(float(sinks[hq]) - m)
         o[hq] = (p @ V[:, h, :]) / z
         lse[hq] = m + math.log(z)
         p_all[hq] = p / z
@@ -182,13 +193,13 @@ def _request_f64(q_i, K, V, q_dtype, kv_dtype, q_scale, k_scale, v_scale):
 def decode_request(q_i, K, V, q_dtype: str, kv_dtype: str, sm_scale: float,
                    logits_soft_cap: float = 0.0, window_left: int = -1,
                    q_scale: float = 1.0, k_scale: float = 1.0,
-                   v_scale: float = 1.0):
+                   v_scale: float = 1.0, sinks=None):
     """Decode attention of one request from its gathered (stored-dtype) K/V."""
     kv_len = K.shape[0]
     s0 = window_start(kv_len, window_left)
     qf, Kf, Vf = _request_f64(q_i, K[s0:], V[s0:], q_dtype, kv_dtype,
                               q_scale, k_scale, v_scale)
-    return attention_state(qf, Kf, Vf, sm_scale, logits_soft_cap)
+    return attention_state(qf, Kf, Vf, sm_scale, logits_soft_cap, sinks=sinks)
 
 
 def _cache_pair(paged_kv_cache):
@@ -201,7 +212,8 @@ def batch_decode(q, paged_kv_cache, layout: str, indptr, indices,
                  last_page_len, page_size: int, q_dtype: str, kv_dtype: str,
                  sm_scale: float, logits_soft_cap: float = 0.0,
                  window_left: int = -1, q_scale: float = 1.0,
-                 k_scale: float = 1.0, v_scale: float = 1.0, requests=None):
+                 k_scale: float = 1.0, v_scale: float = 1.0, requests=None,
+                 sinks=None):
     """o [len(requests), num_qo_heads, head_dim] and lse, both fp64.
 
     ``q`` is [batch, num_qo_heads, head_dim] in its stored dtype;
@@ -219,7 +231,7 @@ def batch_decode(q, paged_kv_cache, layout: str, indptr, indices,
                               int(lens[i]), page_size)
         o[r], lse[r] = decode_request(q[i], K, V, q_dtype, kv_dtype, sm_scale,
                                       logits_soft_cap, window_left, q_scale,
-                                      k_scale, v_scale)
+                                      k_scale, v_scale, sinks)
     return o, lse
 
 
@@ -312,7 +324,7 @@ def batch_decode_multi(q, paged_kv_cache, layout: str, indptr, indices,
                        q_dtype: str, kv_dtype: str, sm_scale: float,
                        logits_soft_cap: float = 0.0, window_left: int = -1,
                        q_scale: float = 1.0, k_scale: float = 1.0,
-                       v_scale: float = 1.0, requests=None):
+                       v_scale: float = 1.0, requests=None, sinks=None):
     """Decode with q_len_per_req query tokens per request, fp64.
 
     ``q`` is [batch * q_len_per_req, num_qo_heads, head_dim] (request-major,
@@ -341,5 +353,5 @@ def batch_decode_multi(q, paged_kv_cache, layout: str, indptr, indices,
             o[r * Q + j], lse[r * Q + j] = decode_request(
                 q[i * Q + j], K[:pos + 1], V[:pos + 1], q_dtype, kv_dtype,
                 sm_scale, logits_soft_cap, window_left, q_scale, k_scale,
-                v_scale)
+                v_scale, sinks)
     return o, lse

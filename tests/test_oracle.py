@@ -558,3 +558,48 @@ def test_block_table_rejects_short_rows():
         oracle.csr_from_block_table([9], np.zeros((1, 2), np.int32), 4)
     with pytest.raises(ValueError):
         oracle.csr_from_block_table([0], np.zeros((1, 2), np.int32), 4)
+
+
+# ------------------------------------------------------------ attention sinks
+
+def test_sink_of_minus_infinity_changes_nothing():
+    rng = np.random.default_rng(21)
+    q, K, V = rng.standard_normal((4, 8)), rng.standard_normal((9, 2, 8)), \
+        rng.standard_normal((9, 2, 8))
+    a = oracle.attention_state(q, K, V, 0.4)
+    b = oracle.attention_state(q, K, V, 0.4, sinks=np.full(4, -np.inf))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_sink_with_zero_query_closed_form():
+    # every logit 0: o = n/(n + e^s) * mean(V), lse = ln(n + e^s)
+    rng = np.random.default_rng(22)
+    n = 13
+    K, V = rng.standard_normal((n, 1, 4)), rng.standard_normal((n, 1, 4))
+    for s in (-3.0, 0.0, 2.5, 40.0):
+        o, lse = oracle.attention_state(np.zeros((2, 4)), K, V, 1.0,
+                                        sinks=np.array([s, s]))
+        z = n + math.exp(s)
+        assert np.allclose(o[0], V[:, 0].sum(0) / z, atol=1e-12)
+        assert abs(lse[0] - math.log(z)) < 1e-12
+
+
+def test_sink_equals_sdpa_with_a_zero_value_key():
+    """The sink acts as one more key whose logit is s and whose value row is
+    zero: SDPA (fp64) over K and V extended by such a row, per q head."""
+    rng = np.random.default_rng(23)
+    nq, nkv, hd, n = 4, 2, 8, 11
+    q = rng.standard_normal((nq, hd))
+    K, V = rng.standard_normal((n, nkv, hd)), rng.standard_normal((n, nkv, hd))
+    sinks = rng.standard_normal(nq) * 2
+    sm = 0.3
+    o, _ = oracle.attention_state(q, K, V, sm, sinks=sinks)
+    for hq in range(nq):
+        h = hq // (nq // nkv)
+        ks = q[hq] * sinks[hq] / (sm * (q[hq] @ q[hq]))   # sm * q.ks = sink
+        Ke = np.concatenate([K[:, h], ks[None]])[None, None]
+        Ve = np.concatenate([V[:, h], np.zeros((1, hd))])[None, None]
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q[hq][None, None, None]),
+                                             torch.from_numpy(Ke), torch.from_numpy(Ve),
+                                             scale=sm)[0, 0, 0].numpy()
+        assert np.max(np.abs(o[hq] - ref)) < 1e-12
