@@ -200,6 +200,12 @@ void pkd_plan_destroy(pkd_plan* plan);
  *            2*P*num_kv_heads*head_dim for the 5-D cache,
  *            P*num_kv_heads*head_dim for a (k_cache, v_cache) pair
  *   q_scale, k_scale, v_scale  calibration scales (1.0 = none)
+ *   sinks    device fp32 [num_qo_heads] (the XQA decode's "sinks"
+ *            [num_kv_heads][G], flattened in q-head order), or NULL: the
+ *            sink s of a q head is one more logit of its softmax, in the
+ *            units of the final logits x and never capped, with no value
+ *            row: o = sum_t e^x_t v_t / (sum_t e^x_t + e^s) and
+ *            lse = ln(sum_t e^x_t + e^s); -inf is no sink
  *   o        device, [B*Q][num_qo_heads][head_dim] in o_dtype, written
  *   lse      device, [B*Q][num_qo_heads] fp32 natural-log LSE, or NULL
  *   workspace, workspace_bytes  device scratch of at least
@@ -221,8 +227,9 @@ void pkd_plan_destroy(pkd_plan* plan);
  * buffer), PKD_EWORKSPACE, PKD_EHIP (launch failure). */
 pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
                    const void* v_cache, int64_t page_stride, float q_scale,
-                   float k_scale, float v_scale, void* o, float* lse,
-                   void* workspace, size_t workspace_bytes, void* stream);
+                   float k_scale, float v_scale, const float* sinks, void* o,
+                   float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream);
 
 /* merge_states (named with fixed_split_size in plan()): combine `num_states`
  * attention states per row by log-sum-exp:

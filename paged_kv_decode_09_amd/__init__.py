@@ -87,7 +87,7 @@ _SIGS = {
     "pkd_plan_get_info": (ctypes.c_int, [_P, ctypes.POINTER(pkd_plan_info)]),
     "pkd_plan_destroy": (None, [_P]),
     "pkd_run": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_float,
-                               ctypes.c_float, ctypes.c_float, _P, _P, _P,
+                               ctypes.c_float, ctypes.c_float, _P, _P, _P, _P,
                                ctypes.c_size_t, _P]),
     "pkd_merge_states": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, _P, ctypes.c_int32, _P,
@@ -350,14 +350,25 @@ class PagedDecodePlan:
 
     def run(self, q: torch.Tensor, paged_kv_cache, q_scale=None, k_scale=None,
             v_scale=None, out=None, lse=None, return_lse: bool = False,
-            workspace: Optional[torch.Tensor] = None, stream=None):
+            workspace: Optional[torch.Tensor] = None, stream=None,
+            sinks: Optional[torch.Tensor] = None):
         """o [B * q_len_per_req, num_qo_heads, head_dim], or (o, lse) when
-        return_lse."""
+        return_lse. ``sinks``: fp32 device tensor of num_qo_heads values
+        ([num_kv_heads, G] or flat), one sink logit per q head."""
         (q, kp, vp, stride, sc, out, lse, ws_ptr, ws_len,
          _ws) = self._args(q, paged_kv_cache, q_scale, k_scale, v_scale, out,
                            lse, return_lse or lse is not None, workspace)
+        sink_ptr = None
+        if sinks is not None:
+            if sinks.dtype != torch.float32 or not sinks.is_cuda or \
+                    not sinks.is_contiguous() or \
+                    sinks.numel() != self.params.num_qo_heads:
+                raise PkdError(PKD_EINVAL, "sinks must be a contiguous fp32 "
+                               f"device tensor of {self.params.num_qo_heads} "
+                               "values")
+            sink_ptr = sinks.data_ptr()
         _check(lib().pkd_run(self._handle, q.data_ptr(), kp, vp, stride,
-                             sc[0], sc[1], sc[2], out.data_ptr(),
+                             sc[0], sc[1], sc[2], sink_ptr, out.data_ptr(),
                              lse.data_ptr() if lse is not None else None,
                              ws_ptr, ws_len, _stream_ptr(stream)))
         return (out, lse) if return_lse else out
@@ -412,7 +423,8 @@ class BatchDecodeWithPagedKVCacheWrapper:
                                    device=self._ws.device)
 
     def run(self, q, paged_kv_cache, q_scale=None, k_scale=None, v_scale=None,
-            out=None, lse=None, return_lse=False, q_len_per_req=None):
+            out=None, lse=None, return_lse=False, q_len_per_req=None,
+            sinks=None):
         if self._plan is None:
             raise PkdError(PKD_EINVAL, "run() before plan()")
         planned = max(1, self._plan.params.q_len_per_req)
@@ -421,7 +433,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
                            f"from the plan's {planned}")
         ws = self._ws if self._plan.workspace_bytes > 0 else None
         return self._plan.run(q, paged_kv_cache, q_scale, k_scale, v_scale,
-                              out, lse, return_lse, ws)
+                              out, lse, return_lse, ws, sinks=sinks)
 
 
 def merge_states(v: torch.Tensor, s: torch.Tensor, out_dtype=None,

@@ -260,8 +260,9 @@ void pkd_plan_destroy(pkd_plan* plan) { free_plan(plan); }
 
 pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
                    const void* v_cache, int64_t page_stride, float q_scale,
-                   float k_scale, float v_scale, void* o, float* lse,
-                   void* workspace, size_t workspace_bytes, void* stream) {
+                   float k_scale, float v_scale, const float* sinks, void* o,
+                   float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   pkd_status st = check_run(plan, q, k_cache, v_cache, page_stride, o, workspace,
                             workspace_bytes);
   if (st != PKD_OK) return st;
@@ -315,6 +316,9 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
   a.inv_cap = cap ? 1.0f / p.logits_soft_cap : 0.0f;
   a.v_scale = v_scale;
   a.steal_limit = plan->host.steal_limit;
+  if (sinks != nullptr && reinterpret_cast<uintptr_t>(sinks) % 4 != 0)
+    return pkd::fail(PKD_EINVAL, "sinks must be 4-byte aligned");
+  a.sinks = sinks;
   int e = pkd::launch_decode(p, a, plan->host.info.num_workgroups, stream);
   if (e != hipSuccess) return hip_fail((hipError_t)e, "decode launch");
   return PKD_OK;

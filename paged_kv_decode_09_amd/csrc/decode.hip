@@ -290,6 +290,17 @@ __device__ void merge_partials(const DecodeArgs& a, int request, int qh0, int fi
       lds_barrier();
     }
     if (!active) continue;
+    if (out_slot < 0 && a.sinks != nullptr) {
+      // the q head's sink joins the final softmax (one more logit, no value)
+      const float s2 = a.sinks[qh0 + gh] * kLog2e;
+      const float Mn = fmaxf(M, s2);
+      if (Mn != -INFINITY) {
+        const float r = M == -INFINITY ? 0.0f : fast_exp2(M - Mn);
+        den = den * r + (s2 == -INFINITY ? 0.0f : fast_exp2(s2 - Mn));
+        num *= r;
+        M = Mn;
+      }
+    }
     const float lse2 = den > 0.0f ? M + __builtin_amdgcn_logf(den) : -INFINITY;
     if (out_slot < 0) {
       const size_t orow = ((size_t)request * a.q_len + qj) * nq + qh0 + gh;
@@ -803,13 +814,24 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
           num += sw * *reinterpret_cast<const f32x4*>(smem + w * G_::kWaveLds + (h * HD + c) * 4);
           den += sw * s_d[w][h];
         }
+        const int qh = qh0 + gh;
+        if (cu.partial < 0 && a.sinks != nullptr) {
+          // the q head's sink joins the softmax (one more logit, no value)
+          const float s2 = a.sinks[qh] * kLog2e;
+          const float Mn = fmaxf(M, s2);
+          if (Mn != -INFINITY) {
+            const float r = M == -INFINITY ? 0.0f : fast_exp2(M - Mn);
+            den = den * r + (s2 == -INFINITY ? 0.0f : fast_exp2(s2 - Mn));
+            num *= r;
+            M = Mn;
+          }
+        }
         // (a row with no visible token in this unit, possible only for an
         // early query token of a split request, is an empty state)
         f32x4 ov;
 #pragma unroll
         for (int i = 0; i < 4; ++i) ov[i] = den > 0.0f ? num[i] / den * a.v_scale : 0.0f;
         const float lse2 = den > 0.0f ? M + __builtin_amdgcn_logf(den) : -INFINITY;
-        const int qh = qh0 + gh;
         if (cu.partial < 0) {
           const size_t orow = ((size_t)cu.request * a.q_len + qj) * a.num_qo_heads + qh;
           store_out4(a.o, orow * HD + c, ov, a.o_bf16);

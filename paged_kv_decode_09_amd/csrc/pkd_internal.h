@@ -149,6 +149,7 @@ struct DecodeArgs {
   float inv_cap;
   float v_scale;
   int32_t steal_limit;  // items below it may be published for stealing
+  const float* sinks;   // NULL, or one sink logit per q head (natural units)
 };
 
 struct MergeArgs {

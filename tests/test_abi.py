@@ -73,7 +73,7 @@ def test_plan_rejects_invalid_input(kw, indptr, last, status, needle):
 def test_run_before_plan_and_bad_merge_args_fail_on_host():
     lib = pkd.lib()
     st = lib.pkd_run(None, None, None, None, 0, 1.0, 1.0, 1.0, None, None,
-                     None, 0, None)
+                     None, None, 0, None)
     assert st == pkd.PKD_EINVAL and b"before plan" in lib.pkd_last_error()
     st = lib.pkd_merge_states(None, None, 4, 2, 0, None, pkd.PKD_F32, None, None)
     assert st == pkd.PKD_EUNSUPPORTED
