@@ -186,6 +186,39 @@ pkd_status pkd_plan_query_block_table(const pkd_plan_params* params, const int32
                                       pkd_plan_info* info, pkd_work_item* items,
                                       int32_t capacity);
 
+/* A graph plan: the CUDAGraph-compatible decode wrapper of the same page
+ * (CUDAGraphBatchDecodeWithPagedKVCacheWrapper: fixed indptr / indices /
+ * last_page_len buffers, a batch size fixed for the wrapper's life, plan()
+ * not capturable). Such a plan keeps its device memory, its launch size (one
+ * workgroup per slot of the GPU; those without a unit exit at once) and its
+ * workspace layout for its whole life, sized for any page table of
+ * params->batch_size requests holding at most max_pages pages, so that a
+ * pkd_run recorded once in a HIP graph serves every later
+ * pkd_plan_update. The kernel reads the current unit count from the plan's
+ * device memory.
+ *   max_pages   capacity of `indices` (entries), >= indptr[B]
+ *   indices     DEVICE, BORROWED for the plan's life; the caller writes each
+ *               page table's page ids into it before (stream order) the
+ *               runs that use them
+ * pkd_plan_info.workspace_bytes is then the capacity's (the same after every
+ * update). Errors as pkd_plan_create, and PKD_EINVAL for batch_size < 1,
+ * max_pages < 1 or a page table with more pages; PKD_EUNSUPPORTED when the
+ * capacity exceeds the 2 GiB workspace or the 2^24 unit limits. */
+pkd_status pkd_plan_create_graph(const pkd_plan_params* params, int32_t max_pages,
+                                 const int32_t* indptr, const int32_t* last_page_len,
+                                 const int32_t* indices, void* stream, pkd_plan** out);
+
+/* A new page table for a graph plan (same parameters and batch size):
+ * plans it on the host, waits for the plan's previous upload, and uploads
+ * the new work list on `stream` into the same device memory. Runs of the
+ * plan must be stream-ordered after it (and none may be running). Not
+ * capturable. Errors: PKD_EINVAL (not a graph plan, NULL, more than
+ * max_pages pages, invalid page table), PKD_EUNSUPPORTED (more units than
+ * the capacity; not expected within max_pages), PKD_EHIP. On error the plan
+ * keeps its previous page table. */
+pkd_status pkd_plan_update(pkd_plan* plan, const int32_t* indptr,
+                           const int32_t* last_page_len, void* stream);
+
 pkd_status pkd_plan_get_info(const pkd_plan* plan, pkd_plan_info* info);
 
 /* Waits for the plan's upload to finish, then frees it. NULL is a no-op. */

@@ -84,6 +84,10 @@ _SIGS = {
                                                   ctypes.c_int32, ctypes.c_int32,
                                                   ctypes.POINTER(pkd_plan_info), _P,
                                                   ctypes.c_int32]),
+    "pkd_plan_create_graph": (ctypes.c_int, [ctypes.POINTER(pkd_plan_params),
+                                             ctypes.c_int32, _P, _P, _P, _P,
+                                             ctypes.POINTER(_P)]),
+    "pkd_plan_update": (ctypes.c_int, [_P, _P, _P, _P]),
     "pkd_plan_get_info": (ctypes.c_int, [_P, ctypes.POINTER(pkd_plan_info)]),
     "pkd_plan_destroy": (None, [_P]),
     "pkd_run": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_float,
@@ -260,7 +264,12 @@ class PagedDecodePlan:
                  fixed_split_size: Optional[int] = None,
                  disable_split_kv: bool = False, stream=None,
                  q_len_per_req: int = 1, seq_lens=None,
-                 block_tables: Optional[torch.Tensor] = None):
+                 block_tables: Optional[torch.Tensor] = None,
+                 graph_max_pages: Optional[int] = None):
+        """``graph_max_pages``: make a graph plan (pkd_plan_create_graph) whose
+        device memory, launch size and workspace layout hold for any later
+        page table of the same batch size with at most that many pages
+        (``update``); ``indices`` is then the fixed page index buffer."""
         self._handle = None
         table = block_tables if block_tables is not None else indices
         if table is None or table.dtype != torch.int32 or not table.is_cuda:
@@ -289,7 +298,14 @@ class PagedDecodePlan:
                                   disable_split_kv, q_len_per_req)
         self.indices = table.contiguous()   # borrowed by the plan: keep alive
         h = _P()
-        if block_tables is not None:
+        if graph_max_pages is not None:
+            if block_tables is not None:
+                raise PkdError(PKD_EINVAL, "a graph plan takes a CSR page table")
+            _check(lib().pkd_plan_create_graph(
+                ctypes.byref(self.params), int(graph_max_pages), ip.ctypes.data,
+                lp.ctypes.data, self.indices.data_ptr(), _stream_ptr(stream),
+                ctypes.byref(h)))
+        elif block_tables is not None:
             _check(lib().pkd_plan_create_block_table(
                 ctypes.byref(self.params), sl.ctypes.data,
                 self.indices.data_ptr(), int(self.indices.shape[1]),
@@ -311,6 +327,17 @@ class PagedDecodePlan:
     @property
     def workspace_bytes(self) -> int:
         return int(self.info.workspace_bytes)
+
+    def update(self, indptr, last_page_len, stream=None) -> None:
+        """A graph plan's new page table (pkd_plan_update): same batch size,
+        pages already in the plan's index buffer. Not capturable."""
+        ip, lp = _host_i32(indptr), _host_i32(last_page_len)
+        if len(lp) != self.params.batch_size or len(ip) != len(lp) + 1:
+            raise PkdError(PKD_EINVAL, "a graph plan keeps its batch size "
+                           f"({self.params.batch_size})")
+        _check(lib().pkd_plan_update(self._handle, ip.ctypes.data,
+                                     lp.ctypes.data, _stream_ptr(stream)))
+        _check(lib().pkd_plan_get_info(self._handle, ctypes.byref(self.info)))
 
     def _args(self, q, paged_kv_cache, q_scale, k_scale, v_scale, out, lse,
               return_lse, workspace):
@@ -436,6 +463,98 @@ class BatchDecodeWithPagedKVCacheWrapper:
                               out, lse, return_lse, ws, sinks=sinks)
 
 
+class CUDAGraphBatchDecodeWithPagedKVCacheWrapper:
+    """The graph-capturable decode wrapper of the page: the page table lives
+    in fixed device buffers, plan() (not capturable) rewrites them and the
+    plan's work list in place, and a run() captured once in a HIP graph
+    serves every later plan() of the same batch size and parameters.
+
+    ``indices_buffer`` bounds the pages of any batch (max_num_pages);
+    ``indptr_buffer`` / ``last_page_len_buffer`` hold [batch + 1] / [batch].
+    The workspace must hold the plan's capacity-based workspace_bytes.
+    """
+
+    def __init__(self, workspace_buffer: torch.Tensor, indptr_buffer: torch.Tensor,
+                 indices_buffer: torch.Tensor, last_page_len_buffer: torch.Tensor,
+                 kv_layout: str = "NHD", use_tensor_cores: bool = False):
+        for name, t in (("indptr_buffer", indptr_buffer),
+                        ("indices_buffer", indices_buffer),
+                        ("last_page_len_buffer", last_page_len_buffer)):
+            if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+                raise PkdError(PKD_EINVAL, f"{name} must be a contiguous int32 "
+                               "device tensor")
+        self._ws = workspace_buffer
+        self._indptr_buf = indptr_buffer
+        self._indices_buf = indices_buffer
+        self._last_buf = last_page_len_buffer
+        self._layout = kv_layout
+        self._plan: Optional[PagedDecodePlan] = None
+        self._key = None
+
+    def plan(self, indptr, indices, last_page_len, num_qo_heads, num_kv_heads,
+             head_dim, page_size, pos_encoding_mode="NONE", window_left=-1,
+             logits_soft_cap=None, q_data_type=torch.float16,
+             kv_data_type=None, o_data_type=None, data_type=None,
+             sm_scale=None, rope_scale=None, rope_theta=None,
+             non_blocking=True, fixed_split_size=None,
+             disable_split_kv=False, q_len_per_req=1) -> None:
+        if pos_encoding_mode != "NONE":
+            raise PkdError(PKD_EUNSUPPORTED,
+                           f"pos_encoding_mode {pos_encoding_mode!r}")
+        if data_type is not None:
+            q_data_type = data_type
+            kv_data_type = kv_data_type or data_type
+        ip, lp = _host_i32(indptr), _host_i32(last_page_len)
+        B, n = len(lp), int(ip[-1]) if len(ip) else 0
+        if B + 1 > self._indptr_buf.numel() or B > self._last_buf.numel():
+            raise PkdError(PKD_EINVAL, f"batch {B} exceeds the indptr / "
+                           "last_page_len buffers")
+        if n > self._indices_buf.numel():
+            raise PkdError(PKD_EINVAL, f"{n} pages exceed the indices buffer "
+                           f"({self._indices_buf.numel()})")
+        params = make_params(B, num_qo_heads, num_kv_heads, head_dim, page_size,
+                             self._layout, window_left, logits_soft_cap,
+                             q_data_type, kv_data_type, o_data_type, sm_scale,
+                             fixed_split_size, disable_split_kv, q_len_per_req)
+        key = bytes(params)
+        src = indices if isinstance(indices, torch.Tensor) else \
+            torch.from_numpy(_host_i32(indices))
+        if src.numel() < n:
+            raise PkdError(PKD_EINVAL, f"indices holds {src.numel()} entries, "
+                           f"indptr needs {n}")
+        # plan first (it validates), then the page table into the fixed
+        # buffers; both are ordered before later runs on the current stream
+        if self._plan is None:
+            self._plan = PagedDecodePlan(
+                ip, self._indices_buf, lp, num_qo_heads, num_kv_heads, head_dim,
+                page_size, self._layout, window_left, logits_soft_cap,
+                q_data_type, kv_data_type, o_data_type, sm_scale,
+                fixed_split_size, disable_split_kv, q_len_per_req=q_len_per_req,
+                graph_max_pages=self._indices_buf.numel())
+            self._key = key
+        else:
+            if key != self._key:
+                raise PkdError(PKD_EINVAL, "a graph wrapper keeps its batch size "
+                               "and parameters; create a new wrapper")
+            self._plan.update(ip, lp)
+        self._indptr_buf[:B + 1].copy_(torch.from_numpy(ip), non_blocking=True)
+        self._last_buf[:B].copy_(torch.from_numpy(lp), non_blocking=True)
+        self._indices_buf[:n].copy_(src[:n].to(torch.int32), non_blocking=True)
+        need = self._plan.workspace_bytes
+        if self._ws.numel() * self._ws.element_size() < need:
+            raise PkdError(PKD_EWORKSPACE, f"workspace of "
+                           f"{self._ws.numel() * self._ws.element_size()} bytes "
+                           f"< {need} needed by the graph plan's capacity")
+
+    def run(self, q, paged_kv_cache, q_scale=None, k_scale=None, v_scale=None,
+            out=None, lse=None, return_lse=False, sinks=None):
+        if self._plan is None:
+            raise PkdError(PKD_EINVAL, "run() before plan()")
+        ws = self._ws if self._plan.workspace_bytes > 0 else None
+        return self._plan.run(q, paged_kv_cache, q_scale, k_scale, v_scale,
+                              out, lse, return_lse, ws, sinks=sinks)
+
+
 def merge_states(v: torch.Tensor, s: torch.Tensor, out_dtype=None,
                  stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Merge attention states (pkd_merge_states).
@@ -459,6 +578,8 @@ def merge_states(v: torch.Tensor, s: torch.Tensor, out_dtype=None,
 
 
 __all__ = ["lib", "PkdError", "PagedDecodePlan",
-           "BatchDecodeWithPagedKVCacheWrapper", "merge_states", "plan_query",
+           "BatchDecodeWithPagedKVCacheWrapper",
+           "CUDAGraphBatchDecodeWithPagedKVCacheWrapper", "merge_states",
+           "plan_query",
            "plan_query_block_table",
            "make_params", "pkd_plan_params", "pkd_plan_info", "pkd_work_item"]

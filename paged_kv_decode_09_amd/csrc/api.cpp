@@ -19,11 +19,23 @@ struct pkd_plan {
   void* staging = nullptr;            // pinned host copy used by the upload
   hipEvent_t uploaded = nullptr;
   int device = 0;
+  int32_t slots = 0;                  // decode workgroups that fit on the GPU
+  // A graph plan (pkd_plan_create_graph) keeps its device memory, its launch
+  // size and its workspace layout for its whole life, sized for capacities;
+  // pkd_plan_update rewrites the contents, and the kernel reads the item
+  // count, the stealing limit and the merge-counter stride from the header.
+  bool graph = false;
+  int32_t max_pages = 0;              // capacity of the page index buffer
+  int32_t cap_items = 0;
+  int32_t cap_partials = 0;
+  int32_t cap_merge_stride = 0;
   // Device copy, all uploaded from the staging copy: the work counters
-  // (zeros), the reserve slots (0xFFFFFFFF: never published), the
-  // per-(request, kv head) merge counters (zeros), the items.
+  // (zeros) and the header, the reserve slots (0xFFFFFFFF: never published),
+  // the per-(request, kv head) merge counters (zeros), the items.
   static constexpr size_t kCounterBytes = 64;
+  static constexpr int kHeaderWord = 4;   // header: int32 words 4, 5, 6
   int32_t merge_stride() const {
+    if (graph) return cap_merge_stride;
     return 1 + (host.max_units + pkd::kMergeGroup - 1) / pkd::kMergeGroup;
   }
   size_t merge_counter_bytes() const {
@@ -34,6 +46,8 @@ struct pkd_plan {
   size_t reserve_bytes() const {
     return ((size_t)host.info.num_workgroups * 2 * 4 + 63) & ~(size_t)63;   // two per workgroup
   }
+  size_t item_capacity() const { return graph ? (size_t)cap_items : host.items.size(); }
+  int32_t ws_partials() const { return graph ? cap_partials : host.info.num_partials; }
   int32_t* d_counters() const { return reinterpret_cast<int32_t*>(dev); }
   int32_t* d_reserve() const {
     return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(dev) + kCounterBytes);
@@ -67,9 +81,42 @@ void free_plan(pkd_plan* p) {
 }
 
 size_t plan_bytes(const pkd_plan& p) {
-  if (p.host.items.empty()) return 0;
+  if (p.item_capacity() == 0) return 0;
   return pkd_plan::kCounterBytes + p.reserve_bytes() + p.merge_counter_bytes() +
-         p.host.items.size() * sizeof(pkd_work_item);
+         p.item_capacity() * sizeof(pkd_work_item);
+}
+
+// Fills the staging copy from the host plan and uploads it on `stream`
+// (after the previous upload from the same staging memory has finished).
+pkd_status upload(pkd_plan* p, void* stream) {
+  const size_t bytes = plan_bytes(*p);
+  if (bytes == 0) return PKD_OK;
+  hipError_t e;
+  if (p->uploaded != nullptr) {
+    e = hipEventSynchronize(p->uploaded);
+    if (e != hipSuccess) return hip_fail(e, "waiting for the previous upload");
+  }
+  char* s = reinterpret_cast<char*>(p->staging);
+  std::memset(s, 0, pkd_plan::kCounterBytes);
+  int32_t* header = reinterpret_cast<int32_t*>(s) + pkd_plan::kHeaderWord;
+  header[0] = p->host.info.num_items;
+  header[1] = p->host.steal_limit;
+  header[2] = p->merge_stride();
+  std::memset(s + pkd_plan::kCounterBytes, 0xFF, p->reserve_bytes());
+  const size_t zeros = pkd_plan::kCounterBytes + p->reserve_bytes();
+  std::memset(s + zeros, 0, p->merge_counter_bytes());
+  std::memcpy(s + zeros + p->merge_counter_bytes(), p->host.items.data(),
+              p->host.items.size() * sizeof(pkd_work_item));
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  e = hipMemcpyAsync(p->dev, p->staging, bytes, hipMemcpyHostToDevice, hs);
+  if (e == hipSuccess && p->uploaded == nullptr)
+    e = hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(p->uploaded, hs);
+  if (e != hipSuccess) {
+    (void)hipStreamSynchronize(hs);
+    return hip_fail(e, "uploading the work list");
+  }
+  return PKD_OK;
 }
 
 pkd_status check_run(const pkd_plan* plan, const void* q, const void* k,
@@ -133,9 +180,32 @@ pkd_status query_plan(const pkd_plan_params* params, const int32_t* indptr,
   return PKD_OK;
 }
 
+// Capacities of a graph plan for B requests holding at most max_pages pages
+// in all: units per kv head (all requests, and one request) from the
+// planner's rules (at most one unit per started chunk and sub-chunk under a
+// fixed split; units of at least kUnitQuantum tokens under its own split).
+void graph_capacities(const pkd_plan_params& p, int32_t max_pages, int64_t* units_total,
+                      int64_t* units_one) {
+  const int64_t B = p.batch_size, P = p.page_size, M = max_pages;
+  if (p.disable_split_kv) {
+    *units_total = B;
+    *units_one = 1;
+  } else if (p.fixed_split_size > 0) {
+    const int64_t S = p.fixed_split_size;
+    const int64_t cap = std::min<int64_t>(S * P, pkd::kFixedUnitMaxTokens);
+    const int64_t sub = (S * P + cap - 1) / cap;
+    *units_total = (M / S + B) * sub;
+    *units_one = (M / S + 1) * sub;
+  } else {
+    *units_total = M * P / pkd::kUnitQuantumTokens + B;
+    *units_one = M * P / pkd::kUnitQuantumTokens + 1;
+  }
+}
+
 pkd_status create_plan(const pkd_plan_params* params, const int32_t* indptr,
                        const int32_t* last_page_len, const int32_t* page_base,
-                       const int32_t* indices, void* stream, pkd_plan** out) {
+                       const int32_t* indices, void* stream, pkd_plan** out,
+                       int32_t graph_max_pages = 0) {
   pkd_status st = pkd::check_params(*params);
   if (st != PKD_OK) return st;
   if (params->batch_size > 0 && indices == nullptr)
@@ -153,7 +223,8 @@ pkd_status create_plan(const pkd_plan_params* params, const int32_t* indptr,
   if (per_cu < 1) return pkd::fail(PKD_EHIP, "occupancy query of the decode kernel failed");
   pkd_plan* p = new (std::nothrow) pkd_plan();
   if (p == nullptr) return pkd::fail(PKD_ENOMEM, "plan allocation failed");
-  st = pkd::build_host_plan(*params, indptr, last_page_len, cus * per_cu, &p->host, page_base);
+  p->slots = cus * per_cu;
+  st = pkd::build_host_plan(*params, indptr, last_page_len, p->slots, &p->host, page_base);
   if (st == PKD_OK) p->host.info.workgroups_per_cu = per_cu;
   if (st != PKD_OK) {
     delete p;
@@ -161,6 +232,31 @@ pkd_status create_plan(const pkd_plan_params* params, const int32_t* indptr,
   }
   p->indices = indices;
   p->device = dev;
+  if (graph_max_pages > 0) {
+    int64_t total = 0, one = 0;
+    graph_capacities(*params, graph_max_pages, &total, &one);
+    const int64_t items = total * params->num_kv_heads;
+    const int64_t stride = 1 + (one + pkd::kMergeGroup - 1) / pkd::kMergeGroup;
+    const int32_t Q = pkd::q_len_of(*params);
+    if (items >= (int64_t)pkd::kMaxItems ||
+        (int64_t)params->batch_size * params->num_kv_heads * stride * 4 > INT32_MAX / 2 ||
+        total * Q * params->num_qo_heads * params->head_dim * 4 > INT32_MAX) {
+      delete p;
+      return pkd::fail(PKD_EUNSUPPORTED, "graph plan capacity of " +
+                                             std::to_string(graph_max_pages) +
+                                             " pages is too large for this batch");
+    }
+    p->graph = true;
+    p->max_pages = graph_max_pages;
+    p->cap_items = (int32_t)items;
+    p->cap_partials = (int32_t)total;
+    p->cap_merge_stride = (int32_t)stride;
+    // the launch covers every slot: workgroups without a unit exit at once
+    p->host.info.num_workgroups = p->slots;
+    p->host.info.workspace_bytes =
+        pkd::workspace_lse_offset(p->cap_partials, Q * params->num_qo_heads, params->head_dim) +
+        (size_t)p->cap_partials * Q * params->num_qo_heads * 4;
+  }
   const size_t bytes = plan_bytes(*p);
   if (bytes > 0) {
     e = hipMalloc(&p->dev, bytes);
@@ -175,21 +271,10 @@ pkd_status create_plan(const pkd_plan_params* params, const int32_t* indptr,
       return pkd::fail(PKD_ENOMEM, std::string("hipHostMalloc of the staging copy: ") +
                                        hipGetErrorString(e));
     }
-    char* s = reinterpret_cast<char*>(p->staging);
-    std::memset(s, 0, pkd_plan::kCounterBytes);
-    std::memset(s + pkd_plan::kCounterBytes, 0xFF, p->reserve_bytes());
-    const size_t zeros = pkd_plan::kCounterBytes + p->reserve_bytes();
-    std::memset(s + zeros, 0, p->merge_counter_bytes());
-    std::memcpy(s + zeros + p->merge_counter_bytes(), p->host.items.data(),
-                p->host.items.size() * sizeof(pkd_work_item));
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    e = hipMemcpyAsync(p->dev, p->staging, bytes, hipMemcpyHostToDevice, hs);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventRecord(p->uploaded, hs);
-    if (e != hipSuccess) {
-      (void)hipStreamSynchronize(hs);
+    st = upload(p, stream);
+    if (st != PKD_OK) {
       free_plan(p);
-      return hip_fail(e, "uploading the work list");
+      return st;
     }
   }
   *out = p;
@@ -249,6 +334,51 @@ pkd_status pkd_plan_create_block_table(const pkd_plan_params* params, const int3
                      out);
 }
 
+pkd_status pkd_plan_create_graph(const pkd_plan_params* params, int32_t max_pages,
+                                 const int32_t* indptr, const int32_t* last_page_len,
+                                 const int32_t* indices, void* stream, pkd_plan** out) {
+  if (out == nullptr) return pkd::fail(PKD_EINVAL, "out must not be NULL");
+  *out = nullptr;
+  if (params == nullptr) return pkd::fail(PKD_EINVAL, "params must not be NULL");
+  if (params->batch_size < 1)
+    return pkd::fail(PKD_EINVAL, "a graph plan needs batch_size >= 1");
+  if (max_pages < 1) return pkd::fail(PKD_EINVAL, "max_pages " + std::to_string(max_pages) + " < 1");
+  if (indptr != nullptr && indptr[params->batch_size] > max_pages)
+    return pkd::fail(PKD_EINVAL, "the page table holds " +
+                                     std::to_string(indptr[params->batch_size]) +
+                                     " pages > max_pages " + std::to_string(max_pages));
+  return create_plan(params, indptr, last_page_len, nullptr, indices, stream, out, max_pages);
+}
+
+pkd_status pkd_plan_update(pkd_plan* plan, const int32_t* indptr, const int32_t* last_page_len,
+                           void* stream) {
+  if (plan == nullptr) return pkd::fail(PKD_EINVAL, "plan is NULL");
+  if (!plan->graph)
+    return pkd::fail(PKD_EINVAL, "pkd_plan_update needs a plan from pkd_plan_create_graph");
+  const pkd_plan_params& p = plan->host.params;
+  if (indptr == nullptr || last_page_len == nullptr)
+    return pkd::fail(PKD_EINVAL, "indptr / last_page_len must not be NULL");
+  if (indptr[p.batch_size] > plan->max_pages)
+    return pkd::fail(PKD_EINVAL, "the page table holds " + std::to_string(indptr[p.batch_size]) +
+                                     " pages > max_pages " + std::to_string(plan->max_pages));
+  pkd::HostPlan h;
+  pkd_status st = pkd::build_host_plan(p, indptr, last_page_len, plan->slots, &h);
+  if (st != PKD_OK) return st;
+  const int32_t stride = 1 + (h.max_units + pkd::kMergeGroup - 1) / pkd::kMergeGroup;
+  if (h.info.num_items > plan->cap_items || h.info.num_partials > plan->cap_partials ||
+      stride > plan->cap_merge_stride)
+    return pkd::fail(PKD_EUNSUPPORTED, "the page table needs more units than the graph "
+                                       "plan's capacity (an internal bound was exceeded)");
+  h.info.num_workgroups = plan->slots;
+  h.info.workgroups_per_cu = plan->host.info.workgroups_per_cu;
+  h.info.workspace_bytes = plan->host.info.workspace_bytes;
+  plan->host = std::move(h);
+  st = upload(plan, stream);
+  if (st != PKD_OK) return st;
+  pkd::clear_error();
+  return PKD_OK;
+}
+
 pkd_status pkd_plan_get_info(const pkd_plan* plan, pkd_plan_info* info) {
   if (plan == nullptr || info == nullptr)
     return pkd::fail(PKD_EINVAL, "plan and info must not be NULL");
@@ -267,7 +397,7 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
                             workspace_bytes);
   if (st != PKD_OK) return st;
   const pkd_plan_params& p = plan->host.params;
-  if (plan->host.items.empty()) return PKD_OK;
+  if (plan->item_capacity() == 0) return PKD_OK;
   if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return pkd::fail(PKD_EINVAL, "q_scale, k_scale and v_scale must be finite");
   pkd::DecodeArgs a{};
@@ -283,7 +413,7 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
   a.items = plan->d_items();
   a.o = o;
   a.lse = lse;
-  const int32_t parts = plan->host.info.num_partials;
+  const int32_t parts = plan->ws_partials();
   a.ws_o = reinterpret_cast<float*>(workspace);
   const int32_t Q = pkd::q_len_of(p);
   a.ws_o_bytes = (size_t)parts * Q * p.num_qo_heads * p.head_dim * 4;
@@ -316,6 +446,7 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
   a.inv_cap = cap ? 1.0f / p.logits_soft_cap : 0.0f;
   a.v_scale = v_scale;
   a.steal_limit = plan->host.steal_limit;
+  a.plan_header = plan->graph ? plan->d_counters() + pkd_plan::kHeaderWord : nullptr;
   if (sinks != nullptr && reinterpret_cast<uintptr_t>(sinks) % 4 != 0)
     return pkd::fail(PKD_EINVAL, "sinks must be 4-byte aligned");
   a.sinks = sinks;

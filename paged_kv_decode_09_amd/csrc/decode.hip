@@ -352,7 +352,15 @@ struct Win {
 };
 
 template <int HD, bool QBF16, bool KV8, bool CAP>
-__global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void decode_kernel(DecodeArgs args) {
+  DecodeArgs a = args;
+  if (args.plan_header != nullptr) {
+    // a graph plan: the launch was recorded once; the current page table's
+    // counts are in the plan's device header
+    a.num_items = __builtin_amdgcn_readfirstlane(args.plan_header[0]);
+    a.steal_limit = __builtin_amdgcn_readfirstlane(args.plan_header[1]);
+    a.merge_stride = __builtin_amdgcn_readfirstlane(args.plan_header[2]);
+  }
   using G_ = Geo<HD, KV8>;
   using O = Op<QBF16>;
   using v8 = typename O::v8;
@@ -628,6 +636,8 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   };
 
   for (;;) {
+    // (a graph plan's launch may hold more workgroups than units)
+    if (cur >= a.num_items) break;
     // ---- chain start: cur's item, first page window and first step, its q,
     // and the item of nxt
     cu = unit_from_lanes(load_item_lanes(a.items, cur, lane));

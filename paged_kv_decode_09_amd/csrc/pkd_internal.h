@@ -18,6 +18,11 @@ constexpr int kWaves = 4;
 constexpr int kStepTokens = 32;
 constexpr int kMaxGroup = 16;       // query rows per kv head: G * Q (one MFMA tile)
 constexpr int kMergeRowsPerBlock = 4;
+// Units the planner sizes itself are multiples of kUnitQuantumTokens tokens
+// (two 32-token steps for each wavefront) and never shorter; under a fixed
+// split, chunks are processed as units of at most kFixedUnitMaxTokens tokens.
+constexpr int kUnitQuantumTokens = 2 * kWaves * kStepTokens;
+constexpr int kFixedUnitMaxTokens = 3072;
 // Units of a split request are merged in two levels: each run of
 // kMergeGroup consecutive units of a (request, kv head) first, then the runs.
 constexpr int kMergeGroup = 8;
@@ -150,6 +155,9 @@ struct DecodeArgs {
   float v_scale;
   int32_t steal_limit;  // items below it may be published for stealing
   const float* sinks;   // NULL, or one sink logit per q head (natural units)
+  // NULL, or (a graph plan) the device words {num_items, steal_limit,
+  // merge_stride} of the current page table, read in place of the above
+  const int32_t* plan_header;
 };
 
 struct MergeArgs {

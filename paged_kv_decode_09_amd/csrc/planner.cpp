@@ -49,7 +49,7 @@ constexpr int kUnitsPerWorkgroup = 4;
 // Units the planner sizes itself are multiples of this many tokens: two steps
 // for each wavefront of a workgroup, so that every wavefront runs an even
 // number of steps (its loop takes steps in pairs).
-constexpr int kUnitQuantum = 2 * kWaves * kStepTokens;
+constexpr int kUnitQuantum = kUnitQuantumTokens;
 // Smallest unit the planner creates on its own, in tokens.
 constexpr int kMinUnitTokens = kUnitQuantum;
 // Under a fixed split, chunks longer than this are processed as sub-chunks of
@@ -58,7 +58,7 @@ constexpr int kMinUnitTokens = kUnitQuantum;
 // request's own length, so results stay batch invariant. A chunk of 4096
 // tokens becomes a unit of 3072 and one of 1024: the short units, taken
 // last, even out the workgroups' ends better than two units of 2048.
-constexpr int kMaxUnitTokens = 3072;
+constexpr int kMaxUnitTokens = kFixedUnitMaxTokens;
 
 }  // namespace
 

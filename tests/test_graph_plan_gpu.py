@@ -1,0 +1,119 @@
+"""GPU tests of graph plans (pkd_plan_create_graph / pkd_plan_update), the
+CUDAGraph-compatible decode wrapper of the API page: one run() captured in a
+HIP graph serves later plan() calls of the same batch size. Every replay
+must give the bits of an ordinary plan's eager run on the same inputs.
+Every test prints its case before it touches the GPU."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_decode_09_amd as pkd
+from paged_kv_decode_09_amd import workloads as wl
+from helpers import LSE_TOL, max_abs, o_tol, oracle_for, plan_for
+
+pytestmark = pytest.mark.gpu
+
+POOL = 600     # pool pages shared by every page table of a test
+MAX_PAGES = 500
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def tables(w, seeds):
+    """Page tables of w.batch requests drawn from one pool (lengths differ
+    per seed; every table fits MAX_PAGES pages)."""
+    out = []
+    for sd in seeds:
+        rng = np.random.default_rng(sd)
+        lengths = rng.integers(w.q_len_per_req, 1200, w.batch)
+        lengths[sd % w.batch] = w.q_len_per_req        # the shortest possible
+        pt = wl.page_table_for(lengths, w.page_size, "perm_pool", rng, POOL)
+        assert pt.indptr[-1] <= MAX_PAGES
+        q = wl.make_q(w, rng, 1.0, "cuda")
+        out.append((pt, q))
+    return out
+
+
+@pytest.mark.parametrize("split,Q", [(None, 1), (2, 1), ("off", 1), (None, 2)])
+def test_graph_replays_follow_each_new_plan(split, Q):
+    w = wl.small_workload(seed=79, batch=6, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                          q_dtype="bf16", kv_dtype="bf16", o_dtype="bf16", layout="HND",
+                          q_len_per_req=Q, pages="perm_pool", pool_pages=POOL)
+    say(w, "split", split)
+    pool = wl.make_pool(w, POOL, "cuda")
+    kw = dict(q_data_type=torch.bfloat16, q_len_per_req=Q,
+              fixed_split_size=split if isinstance(split, int) else None,
+              disable_split_kv=split == "off")
+    dev = "cuda"
+    wrapper = pkd.CUDAGraphBatchDecodeWithPagedKVCacheWrapper(
+        torch.empty(64 << 20, dtype=torch.uint8, device=dev),
+        torch.empty(w.batch + 1, dtype=torch.int32, device=dev),
+        torch.empty(MAX_PAGES, dtype=torch.int32, device=dev),
+        torch.empty(w.batch, dtype=torch.int32, device=dev), kv_layout="HND")
+    cases = tables(w, [1, 2, 3, 4])
+    rows = w.batch * Q
+    q_static = torch.empty((rows, 8, 128), dtype=torch.bfloat16, device=dev)
+    o_static = torch.empty((rows, 8, 128), dtype=torch.bfloat16, device=dev)
+    l_static = torch.empty((rows, 8), dtype=torch.float32, device=dev)
+    pt0, q0 = cases[0]
+    wrapper.plan(pt0.indptr, torch.from_numpy(pt0.indices).to(dev), pt0.last_page_len,
+                 8, 2, 128, 16, **kw)
+    q_static.copy_(q0)
+    wrapper.run(q_static, pool, out=o_static, lse=l_static)   # warm-up, eager
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wrapper.run(q_static, pool, out=o_static, lse=l_static)
+    torch.cuda.synchronize()
+    for k, (pt, q) in enumerate(cases + cases[:1]):
+        say("page table", k, "pages", int(pt.indptr[-1]))
+        wrapper.plan(pt.indptr, torch.from_numpy(pt.indices).to(dev), pt.last_page_len,
+                     8, 2, 128, 16, **kw)
+        q_static.copy_(q)
+        o_static.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        # an ordinary plan of the same page table, run eagerly
+        idx = torch.from_numpy(pt.indices).to(dev)
+        plain = pkd.PagedDecodePlan(pt.indptr, idx, pt.last_page_len, 8, 2, 128, 16,
+                                    kv_layout="HND", **kw)
+        o_ref, l_ref = plain.run(q, pool, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o_static, o_ref) and torch.equal(l_static, l_ref), k
+    # and against the oracle, for the last table
+    case = wl.Case(replace(w, batch=6), pt, q, pool)
+    ref_o, ref_l = oracle_for(case.w, case)
+    assert max_abs(o_static, ref_o) <= o_tol(w) and max_abs(l_static, ref_l) <= LSE_TOL
+
+
+def test_graph_plan_rejects_what_it_cannot_hold():
+    w = wl.small_workload(seed=83, batch=3, lengths=("fixed", [40, 50, 60]), pool_pages=50,
+                          pages="perm_pool")
+    say(w)
+    case = wl.make_case(w, device="cuda")
+    dev = "cuda"
+    wrapper = pkd.CUDAGraphBatchDecodeWithPagedKVCacheWrapper(
+        torch.empty(1 << 20, dtype=torch.uint8, device=dev),
+        torch.empty(4, dtype=torch.int32, device=dev),
+        torch.empty(12, dtype=torch.int32, device=dev),
+        torch.empty(3, dtype=torch.int32, device=dev))
+    idx = torch.from_numpy(case.pt.indices).to(dev)
+    wrapper.plan(case.pt.indptr, idx, case.pt.last_page_len, 8, 2, 64, 16)
+    # more pages than the indices buffer
+    with pytest.raises(pkd.PkdError):
+        wrapper.plan([0, 5, 10, 15], torch.zeros(15, dtype=torch.int32), [16, 16, 16],
+                     8, 2, 64, 16)
+    # another batch size or other parameters
+    with pytest.raises(pkd.PkdError):
+        wrapper.plan([0, 1, 2], torch.zeros(2, dtype=torch.int32), [3, 3], 8, 2, 64, 16)
+    with pytest.raises(pkd.PkdError):
+        wrapper.plan(case.pt.indptr, idx, case.pt.last_page_len, 8, 2, 64, 16,
+                     window_left=5)
+    # an ordinary plan has no update
+    plain = plan_for(w, case)
+    with pytest.raises(pkd.PkdError):
+        pkd._check(pkd.lib().pkd_plan_update(plain._handle, None, None, None))
