@@ -10,6 +10,7 @@ from .oracle import (
     widen,
     kv_lengths,
     csr_from_block_table,
+    alibi_slopes,
     window_start,
     gather_request,
     attention_state,
@@ -28,6 +29,7 @@ __all__ = [
     "widen",
     "kv_lengths",
     "csr_from_block_table",
+    "alibi_slopes",
     "window_start",
     "gather_request",
     "attention_state",

@@ -36,6 +36,13 @@ unless stated otherwise):
 * Split-KV (plan() parameter fixed_split_size, "in pages"): the sequence is
   cut into chunks of that many pages; per-chunk states are combined by a
   log-sum-exp merge (the merge_states step named there).
+* Positional encoding ALIBI (plan() parameter pos_encoding_mode, "applied
+  inside the attention kernel"). Readings taken: the slopes of the ALiBi
+  paper over the num_qo_heads q heads (for n a power of two, head h gets
+  2^(-8(h+1)/n); otherwise the n' = 2^floor(log2 n) slopes of that rule,
+  then the odd powers of 2^(-4/n') for the remaining heads), and the bias
+  slope * (t - query position) is added to the scaled logit before the soft
+  cap.
 * Several query tokens per request (run() parameter q_len_per_req, default
   1). Readings taken: q, o and lse hold q_len_per_req consecutive rows per
   request, in token order; query token j of a request sits at position
@@ -113,6 +120,15 @@ def csr_from_block_table(seq_lens, block_tables, page_size: int):
     return indptr, indices, last
 
 
+def alibi_slopes(num_heads: int) -> np.ndarray:
+    """ALiBi slopes of num_heads heads (the geometric sequence of the ALiBi
+    paper; the closest power of two below n, then interleaved extra slopes)."""
+    n2 = 2 ** int(math.floor(math.log2(num_heads)))
+    base = [2.0 ** (-8.0 * (h + 1) / n2) for h in range(n2)]
+    extra = [2.0 ** (-4.0 * (2 * k + 1) / n2) for k in range(num_heads - n2)]
+    return np.array(base + extra, dtype=np.float64)
+
+
 def window_start(kv_len: int, window_left: int) -> int:
     """First attended token of a request whose query sits at kv_len-1."""
     if window_left < 0:
@@ -139,13 +155,16 @@ def gather_request(k_cache, v_cache, layout: str, indices, indptr, i: int,
 
 
 def attention_state(q, K, V, sm_scale: float, logits_soft_cap: float = 0.0,
-                    return_weights: bool = False, sinks=None):
+                    return_weights: bool = False, sinks=None, bias=None):
     """Dense softmax attention of one query row per q head over n tokens.
 
     q: [num_qo_heads, head_dim]; K, V: [n, num_kv_heads, head_dim]; all fp64.
     Returns (o [num_qo_heads, head_dim], lse [num_qo_heads]) and, if asked,
     the weights p [num_qo_heads, n]. With n == 0 the state is empty:
     o = 0, lse = -inf.
+
+    ``bias`` (optional, [num_qo_heads, n]): added to the scaled logits before
+    the soft cap (the ALiBi bias).
 
     ``sinks`` (optional, [num_qo_heads]): the attention-sink values of the
     XQA decode on the API page ("sinks" [num_kv_heads, head_group_ratio]
@@ -170,6 +189,8 @@ def attention_state(q, K, V, sm_scale: float, logits_soft_cap: float = 0.0,
     for hq in range(nq):
         h = hq // group
         x = sm_scale * (K[:, h, :] @ q[hq])
+        if bias is not None:
+            x = x + bias[hq]
         if logits_soft_cap > 0:
             x = logits_soft_cap * np.tanh(x / logits_soft_cap)
         m = x.max()
@@ -193,13 +214,19 @@ def _request_f64(q_i, K, V, q_dtype, kv_dtype, q_scale, k_scale, v_scale):
 def decode_request(q_i, K, V, q_dtype: str, kv_dtype: str, sm_scale: float,
                    logits_soft_cap: float = 0.0, window_left: int = -1,
                    q_scale: float = 1.0, k_scale: float = 1.0,
-                   v_scale: float = 1.0, sinks=None):
+                   v_scale: float = 1.0, sinks=None, alibi: bool = False):
     """Decode attention of one request from its gathered (stored-dtype) K/V."""
     kv_len = K.shape[0]
     s0 = window_start(kv_len, window_left)
     qf, Kf, Vf = _request_f64(q_i, K[s0:], V[s0:], q_dtype, kv_dtype,
                               q_scale, k_scale, v_scale)
-    return attention_state(qf, Kf, Vf, sm_scale, logits_soft_cap, sinks=sinks)
+    bias = None
+    if alibi:
+        # the query sits at kv_len - 1; token t is (kv_len - 1 - t) behind it
+        dist = np.arange(s0, kv_len, dtype=np.float64) - (kv_len - 1)
+        bias = alibi_slopes(qf.shape[0])[:, None] * dist[None, :]
+    return attention_state(qf, Kf, Vf, sm_scale, logits_soft_cap, sinks=sinks,
+                           bias=bias)
 
 
 def _cache_pair(paged_kv_cache):
@@ -213,7 +240,7 @@ def batch_decode(q, paged_kv_cache, layout: str, indptr, indices,
                  sm_scale: float, logits_soft_cap: float = 0.0,
                  window_left: int = -1, q_scale: float = 1.0,
                  k_scale: float = 1.0, v_scale: float = 1.0, requests=None,
-                 sinks=None):
+                 sinks=None, alibi: bool = False):
     """o [len(requests), num_qo_heads, head_dim] and lse, both fp64.
 
     ``q`` is [batch, num_qo_heads, head_dim] in its stored dtype;
@@ -231,7 +258,7 @@ def batch_decode(q, paged_kv_cache, layout: str, indptr, indices,
                               int(lens[i]), page_size)
         o[r], lse[r] = decode_request(q[i], K, V, q_dtype, kv_dtype, sm_scale,
                                       logits_soft_cap, window_left, q_scale,
-                                      k_scale, v_scale, sinks)
+                                      k_scale, v_scale, sinks, alibi)
     return o, lse
 
 
@@ -324,7 +351,8 @@ def batch_decode_multi(q, paged_kv_cache, layout: str, indptr, indices,
                        q_dtype: str, kv_dtype: str, sm_scale: float,
                        logits_soft_cap: float = 0.0, window_left: int = -1,
                        q_scale: float = 1.0, k_scale: float = 1.0,
-                       v_scale: float = 1.0, requests=None, sinks=None):
+                       v_scale: float = 1.0, requests=None, sinks=None,
+                       alibi: bool = False):
     """Decode with q_len_per_req query tokens per request, fp64.
 
     ``q`` is [batch * q_len_per_req, num_qo_heads, head_dim] (request-major,
@@ -353,5 +381,5 @@ def batch_decode_multi(q, paged_kv_cache, layout: str, indptr, indices,
             o[r * Q + j], lse[r * Q + j] = decode_request(
                 q[i * Q + j], K[:pos + 1], V[:pos + 1], q_dtype, kv_dtype,
                 sm_scale, logits_soft_cap, window_left, q_scale, k_scale,
-                v_scale, sinks)
+                v_scale, sinks, alibi)
     return o, lse

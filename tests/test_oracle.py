@@ -603,3 +603,46 @@ def test_sink_equals_sdpa_with_a_zero_value_key():
                                              torch.from_numpy(Ke), torch.from_numpy(Ve),
                                              scale=sm)[0, 0, 0].numpy()
         assert np.max(np.abs(o[hq] - ref)) < 1e-12
+
+
+# ------------------------------------------------------------------- ALiBi
+
+def test_alibi_slopes_of_eight_heads_are_the_powers_of_one_half():
+    # the ALiBi paper's example: 8 heads get 1/2, 1/4, ..., 1/256
+    assert np.array_equal(oracle.alibi_slopes(8), 0.5 ** np.arange(1, 9))
+    # 16 heads: 2^-0.5, 2^-1, ..., 2^-8
+    assert np.allclose(oracle.alibi_slopes(16), 2.0 ** (-0.5 * np.arange(1, 17)))
+    # 12 heads: the 8-head slopes, then 2^-1/2^-... odd powers of 2^(-4/8)
+    s12 = oracle.alibi_slopes(12)
+    assert np.array_equal(s12[:8], oracle.alibi_slopes(8))
+    assert np.allclose(s12[8:], 2.0 ** (-0.5 * np.array([1, 3, 5, 7])))
+
+
+@pytest.mark.parametrize("Q,window", [(1, -1), (1, 6), (3, -1), (2, 4)])
+def test_alibi_matches_sdpa_with_a_distance_bias(Q, window):
+    """SDPA (fp64) with a float mask: slope_h * (t - position of the query
+    token), -inf where the causal / window mask hides t."""
+    rng = np.random.default_rng(31 + Q)
+    nkv, group, hd = 2, 4, 8
+    nq = nkv * group
+    lengths = [Q, 14, 33]
+    K = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    V = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    q = rng.standard_normal((len(lengths) * Q, nq, hd))
+    cache, indptr, indices, last = scatter_to_pages(K, V, "HND", 4, 30, rng)
+    o, _ = oracle.batch_decode_multi(q, cache, "HND", indptr, indices, last, 4, Q,
+                                     "f64", "f64", 0.3, window_left=window,
+                                     alibi=True)
+    slopes = oracle.alibi_slopes(nq)
+    for i, L in enumerate(lengths):
+        allowed = prefill_causal_mask(Q, L, window)
+        pos = np.arange(L - Q, L)[:, None]
+        t = np.arange(L)[None, :]
+        bias = slopes[None, :, None, None] * (t - pos)[None, None]   # [1, nq, Q, L]
+        bias = np.where(allowed[None, None], bias, -np.inf)
+        qt = torch.from_numpy(np.ascontiguousarray(q[i * Q:(i + 1) * Q].transpose(1, 0, 2)))[None]
+        kt = torch.from_numpy(np.ascontiguousarray(K[i].transpose(1, 0, 2)))[None]
+        vt = torch.from_numpy(np.ascontiguousarray(V[i].transpose(1, 0, 2)))[None]
+        ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(bias),
+                                             scale=0.3, enable_gqa=True)[0].numpy()
+        assert np.max(np.abs(o[i * Q:(i + 1) * Q] - ref.transpose(1, 0, 2))) < 1e-12
