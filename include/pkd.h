@@ -72,6 +72,14 @@ typedef enum { PKD_F16 = 0, PKD_BF16 = 1, PKD_E4M3 = 2, PKD_F32 = 3 } pkd_dtype;
  * head_dim is always contiguous. */
 typedef enum { PKD_NHD = 0, PKD_HND = 1 } pkd_layout;
 
+/* Positional encoding applied inside the kernel (plan() parameter
+ * pos_encoding_mode). ALIBI adds slope_h * (t - p) to the scaled logit of q
+ * head h for key position t and query position p, before the soft cap; the
+ * slopes are those of the ALiBi paper over num_qo_heads heads: with
+ * n = 2^floor(log2 num_qo_heads), head h < n gets 2^(-8(h+1)/n), head
+ * h >= n gets 2^(-4(2(h-n)+1)/n). */
+typedef enum { PKD_POS_NONE = 0, PKD_POS_ROPE_LLAMA = 1, PKD_POS_ALIBI = 2 } pkd_pos_encoding;
+
 /* Problem description of plan(). Enum-valued fields are int32_t (values from
  * the enums above) so that the struct layout is fixed. */
 typedef struct {
@@ -91,6 +99,10 @@ typedef struct {
   int32_t disable_split_kv; /* nonzero: exactly one chunk per request       */
   int32_t q_len_per_req;    /* Q, query tokens per request; 0 means 1;
                                G*Q <= 16 and every L_i >= Q                 */
+  int32_t pos_encoding_mode; /* pkd_pos_encoding: NONE or ALIBI (ROPE_LLAMA
+                               is rejected with PKD_EUNSUPPORTED)           */
+  float rope_scale;         /* RoPE parameters of plan(); unused unless     */
+  float rope_theta;         /* pos_encoding_mode is ROPE_LLAMA              */
 } pkd_plan_params;
 
 /* One unit of decode work: the tokens [token_begin, token_end) of one chunk of

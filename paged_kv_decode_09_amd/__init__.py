@@ -45,7 +45,9 @@ class pkd_plan_params(ctypes.Structure):
                 ("window_left", ctypes.c_int32),
                 ("fixed_split_size", ctypes.c_int32),
                 ("disable_split_kv", ctypes.c_int32),
-                ("q_len_per_req", ctypes.c_int32)]
+                ("q_len_per_req", ctypes.c_int32),
+                ("pos_encoding_mode", ctypes.c_int32),
+                ("rope_scale", ctypes.c_float), ("rope_theta", ctypes.c_float)]
 
 
 class pkd_work_item(ctypes.Structure):
@@ -142,6 +144,8 @@ def _dtype_code(dt) -> int:
     raise PkdError(PKD_EUNSUPPORTED, f"dtype {dt} is not supported")
 
 
+_POS_MODES = {"NONE": 0, "ROPE_LLAMA": 1, "ALIBI": 2}
+
 _TORCH_OF = {PKD_F16: torch.float16, PKD_BF16: torch.bfloat16,
              PKD_F32: torch.float32}
 
@@ -164,7 +168,8 @@ def make_params(batch_size, num_qo_heads, num_kv_heads, head_dim, page_size,
                 kv_layout="NHD", window_left=-1, logits_soft_cap=None,
                 q_data_type=torch.float16, kv_data_type=None,
                 o_data_type=None, sm_scale=None, fixed_split_size=None,
-                disable_split_kv=False, q_len_per_req=1) -> pkd_plan_params:
+                disable_split_kv=False, q_len_per_req=1, pos_encoding_mode="NONE",
+                rope_scale=None, rope_theta=None) -> pkd_plan_params:
     q_code = _dtype_code(q_data_type)
     kv_code = q_code if kv_data_type is None else _dtype_code(kv_data_type)
     o_code = q_code if o_data_type is None else _dtype_code(o_data_type)
@@ -181,7 +186,11 @@ def make_params(batch_size, num_qo_heads, num_kv_heads, head_dim, page_size,
         window_left=int(window_left),
         fixed_split_size=0 if not fixed_split_size else int(fixed_split_size),
         disable_split_kv=int(bool(disable_split_kv)),
-        q_len_per_req=1 if q_len_per_req is None else int(q_len_per_req))
+        q_len_per_req=1 if q_len_per_req is None else int(q_len_per_req),
+        pos_encoding_mode=_POS_MODES.get(pos_encoding_mode, -1)
+        if isinstance(pos_encoding_mode, str) else int(pos_encoding_mode),
+        rope_scale=1.0 if rope_scale is None else float(rope_scale),
+        rope_theta=1e4 if rope_theta is None else float(rope_theta))
 
 
 def plan_query(indptr, last_page_len, num_cus: int = 256, **kw):
@@ -265,7 +274,9 @@ class PagedDecodePlan:
                  disable_split_kv: bool = False, stream=None,
                  q_len_per_req: int = 1, seq_lens=None,
                  block_tables: Optional[torch.Tensor] = None,
-                 graph_max_pages: Optional[int] = None):
+                 graph_max_pages: Optional[int] = None,
+                 pos_encoding_mode: str = "NONE", rope_scale=None,
+                 rope_theta=None):
         """``graph_max_pages``: make a graph plan (pkd_plan_create_graph) whose
         device memory, launch size and workspace layout hold for any later
         page table of the same batch size with at most that many pages
@@ -295,7 +306,8 @@ class PagedDecodePlan:
                                   page_size, kv_layout, window_left,
                                   logits_soft_cap, q_data_type, kv_data_type,
                                   o_data_type, sm_scale, fixed_split_size,
-                                  disable_split_kv, q_len_per_req)
+                                  disable_split_kv, q_len_per_req,
+                                  pos_encoding_mode, rope_scale, rope_theta)
         self.indices = table.contiguous()   # borrowed by the plan: keep alive
         h = _P()
         if graph_max_pages is not None:
@@ -429,9 +441,6 @@ class BatchDecodeWithPagedKVCacheWrapper:
         """plan() of the page. With ``block_tables`` [B, max_blocks] and
         ``seq_lens`` [B] the page table is a block table; indptr, indices and
         last_page_len are then None."""
-        if pos_encoding_mode != "NONE":
-            raise PkdError(PKD_EUNSUPPORTED,
-                           f"pos_encoding_mode {pos_encoding_mode!r}")
         if data_type is not None:
             q_data_type = data_type
             kv_data_type = kv_data_type or data_type
@@ -441,7 +450,8 @@ class BatchDecodeWithPagedKVCacheWrapper:
             num_kv_heads, head_dim, page_size, self._layout, window_left,
             logits_soft_cap, q_data_type, kv_data_type, o_data_type, sm_scale,
             fixed_split_size, disable_split_kv, q_len_per_req=q_len_per_req,
-            seq_lens=seq_lens,
+            pos_encoding_mode=pos_encoding_mode, rope_scale=rope_scale,
+            rope_theta=rope_theta, seq_lens=seq_lens,
             block_tables=None if block_tables is None else
             block_tables.to(torch.int32))
         need = self._plan.workspace_bytes
@@ -498,9 +508,6 @@ class CUDAGraphBatchDecodeWithPagedKVCacheWrapper:
              sm_scale=None, rope_scale=None, rope_theta=None,
              non_blocking=True, fixed_split_size=None,
              disable_split_kv=False, q_len_per_req=1) -> None:
-        if pos_encoding_mode != "NONE":
-            raise PkdError(PKD_EUNSUPPORTED,
-                           f"pos_encoding_mode {pos_encoding_mode!r}")
         if data_type is not None:
             q_data_type = data_type
             kv_data_type = kv_data_type or data_type
@@ -515,7 +522,8 @@ class CUDAGraphBatchDecodeWithPagedKVCacheWrapper:
         params = make_params(B, num_qo_heads, num_kv_heads, head_dim, page_size,
                              self._layout, window_left, logits_soft_cap,
                              q_data_type, kv_data_type, o_data_type, sm_scale,
-                             fixed_split_size, disable_split_kv, q_len_per_req)
+                             fixed_split_size, disable_split_kv, q_len_per_req,
+                             pos_encoding_mode, rope_scale, rope_theta)
         key = bytes(params)
         src = indices if isinstance(indices, torch.Tensor) else \
             torch.from_numpy(_host_i32(indices))
@@ -530,7 +538,9 @@ class CUDAGraphBatchDecodeWithPagedKVCacheWrapper:
                 page_size, self._layout, window_left, logits_soft_cap,
                 q_data_type, kv_data_type, o_data_type, sm_scale,
                 fixed_split_size, disable_split_kv, q_len_per_req=q_len_per_req,
-                graph_max_pages=self._indices_buf.numel())
+                graph_max_pages=self._indices_buf.numel(),
+                pos_encoding_mode=pos_encoding_mode, rope_scale=rope_scale,
+                rope_theta=rope_theta)
             self._key = key
         else:
             if key != self._key:

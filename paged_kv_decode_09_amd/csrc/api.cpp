@@ -435,6 +435,7 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
   a.q_len = Q;
   a.cols = a.group * Q;
   a.window_left = p.window_left;
+  a.alibi = p.pos_encoding_mode == PKD_POS_ALIBI;
   int lg = 0;
   while ((1 << lg) < p.page_size) ++lg;
   a.log2_page = lg;

@@ -455,6 +455,10 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   // Tokens column n may see in the current unit: up to its query token's
   // position, and from its window start (set per unit).
   int col_lo = 0, col_hi = 0;
+  // ALiBi slope of column n's q head, in the units the logits are in before
+  // the cap (base 2 without a cap); 0 without ALiBi, which leaves every
+  // logit's bits unchanged.
+  float col_slope = 0.0f;
 
   // Attend step s of window W whose K/V rows are in st. A step wholly past
   // the window (the padding step of an odd count) changes nothing.
@@ -493,9 +497,10 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
     for (int tile = 0; tile < 2; ++tile) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float v = sc[tile][i] * a.logit_scale;
-        if constexpr (CAP) v = a.cap * tanh_from_exp(v * a.inv_cap) * kLog2e;
         const int t = t0 + 8 * g + 4 * tile + i;
+        float v = sc[tile][i] * a.logit_scale;
+        v = __builtin_fmaf(col_slope, (float)(t - col_hi), v);   // ALiBi
+        if constexpr (CAP) v = a.cap * tanh_from_exp(v * a.inv_cap) * kLog2e;
         v = (t >= lo && t <= hi) ? v : -INFINITY;
         x[4 * tile + i] = v;
         mx = fmaxf(mx, v);
@@ -679,6 +684,16 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
       d_run = 0.0f;
       col_hi = cu.qpos + col_tok;
       col_lo = a.window_left < 0 ? 0 : col_hi - a.window_left;
+      if (a.alibi) {
+        // the ALiBi paper's slopes over the q heads (n2: the power of two
+        // at or below num_qo_heads; the heads past it take odd powers of
+        // 2^(-4/n2))
+        const int hq = cu.kv_head * group + col_head;
+        const int n2 = 1 << (31 - __builtin_clz(a.num_qo_heads));
+        const float ex = hq < n2 ? -8.0f * (float)(hq + 1) / (float)n2
+                                 : -4.0f * (float)(2 * (hq - n2) + 1) / (float)n2;
+        col_slope = fast_exp2(ex) * (CAP ? 1.0f : kLog2e);
+      }
 #pragma unroll
       for (int b = 0; b < G_::kPvMfma; ++b) acc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
       const int base = cu.tb & ~(kStepTokens - 1);

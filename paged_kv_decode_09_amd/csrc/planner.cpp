@@ -89,6 +89,11 @@ pkd_status check_params(const pkd_plan_params& p) {
     return fail(PKD_EUNSUPPORTED,
                 fmt("group size %d (num_qo_heads/num_kv_heads) exceeds %d",
                     group, kMaxGroup));
+  if (p.pos_encoding_mode == PKD_POS_ROPE_LLAMA)
+    return fail(PKD_EUNSUPPORTED, "pos_encoding_mode ROPE_LLAMA is not built (NONE and ALIBI are)");
+  if (p.pos_encoding_mode != PKD_POS_NONE && p.pos_encoding_mode != PKD_POS_ALIBI)
+    return fail(PKD_EINVAL, fmt("pos_encoding_mode %d is not NONE (0), ROPE_LLAMA (1) or ALIBI (2)",
+                                p.pos_encoding_mode));
   if (p.q_len_per_req < 0)
     return fail(PKD_EINVAL, fmt("q_len_per_req %d < 0", p.q_len_per_req));
   if ((int64_t)group * q_len_of(p) > kMaxGroup)

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_sizes_match_header():
-    assert ctypes.sizeof(pkd.pkd_plan_params) == 15 * 4
+    assert ctypes.sizeof(pkd.pkd_plan_params) == 18 * 4
     assert ctypes.sizeof(pkd.pkd_work_item) == 36
     assert ctypes.sizeof(pkd.pkd_plan_info) == 40
 
@@ -59,6 +59,8 @@ def query(indptr, last, num_cus=256, **kw):
     (dict(q_data_type="float16", kv_data_type="bfloat16"), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "kv_dtype"),
     (dict(o_data_type="float8_e4m3fn"), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "o_dtype"),
     (dict(q_len_per_req=-1), [0, 1], [1], pkd.PKD_EINVAL, "q_len_per_req -1"),
+    (dict(pos_encoding_mode="ROPE_LLAMA"), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "ROPE_LLAMA is not built"),
+    (dict(pos_encoding_mode="XPOS"), [0, 1], [1], pkd.PKD_EINVAL, "pos_encoding_mode -1"),
     (dict(q_len_per_req=5), [0, 1], [8], pkd.PKD_EUNSUPPORTED, "group size 4 x q_len_per_req 5"),
     (dict(q_len_per_req=3), [0, 1, 2], [9, 2], pkd.PKD_EINVAL, "request 1 has kv_len 2 < q_len_per_req 3"),
     (dict(sm_scale=float("inf")), [0, 1], [1], pkd.PKD_EINVAL, "sm_scale"),
