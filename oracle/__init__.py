@@ -11,6 +11,7 @@ from .oracle import (
     kv_lengths,
     csr_from_block_table,
     alibi_slopes,
+    rope_rotate,
     window_start,
     gather_request,
     attention_state,
@@ -30,6 +31,7 @@ __all__ = [
     "kv_lengths",
     "csr_from_block_table",
     "alibi_slopes",
+    "rope_rotate",
     "window_start",
     "gather_request",
     "attention_state",

@@ -43,6 +43,13 @@ unless stated otherwise):
   then the odd powers of 2^(-4/n') for the remaining heads), and the bias
   slope * (t - query position) is added to the scaled logit before the soft
   cap.
+* Positional encoding ROPE_LLAMA (same parameter; rope_scale "used in RoPE
+  interpolation", default 1; rope_theta default 1e4). Readings taken: the
+  Llama-style rotary embedding rotates each pair (x[i], x[i + head_dim/2]),
+  i < head_dim/2, of q (at its query position) and of every key (at its
+  token index) by the angle position / rope_scale * rope_theta^(-2i/head_dim);
+  values are not rotated; the rotation comes before q_scale/k_scale-scaled
+  logits, the ALiBi bias and the cap as the kernel applies it to stored K.
 * Several query tokens per request (run() parameter q_len_per_req, default
   1). Readings taken: q, o and lse hold q_len_per_req consecutive rows per
   request, in token order; query token j of a request sits at position
@@ -118,6 +125,20 @@ def csr_from_block_table(seq_lens, block_tables, page_size: int):
                               enumerate(npages)]).astype(np.int32)
     last = (seq_lens - page_size * (npages - 1)).astype(np.int32)
     return indptr, indices, last
+
+
+def rope_rotate(x, positions, rope_theta: float = 1e4, rope_scale: float = 1.0):
+    """Llama-style rotary embedding of rows x [..., n, head_dim] at the
+    given positions [n] (fp64): pair (i, i + head_dim/2) turns by
+    position / rope_scale * rope_theta^(-2i/head_dim)."""
+    x = np.asarray(x, dtype=np.float64)
+    hd = x.shape[-1]
+    half = hd // 2
+    inv_freq = rope_theta ** (-2.0 * np.arange(half) / hd) / rope_scale
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    lo, hi = x[..., :half], x[..., half:]
+    return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
 
 
 def alibi_slopes(num_heads: int) -> np.ndarray:
@@ -214,12 +235,21 @@ def _request_f64(q_i, K, V, q_dtype, kv_dtype, q_scale, k_scale, v_scale):
 def decode_request(q_i, K, V, q_dtype: str, kv_dtype: str, sm_scale: float,
                    logits_soft_cap: float = 0.0, window_left: int = -1,
                    q_scale: float = 1.0, k_scale: float = 1.0,
-                   v_scale: float = 1.0, sinks=None, alibi: bool = False):
-    """Decode attention of one request from its gathered (stored-dtype) K/V."""
+                   v_scale: float = 1.0, sinks=None, alibi: bool = False,
+                   rope=None):
+    """Decode attention of one request from its gathered (stored-dtype) K/V.
+
+    ``rope`` = (rope_theta, rope_scale) applies ROPE_LLAMA to q (at position
+    kv_len - 1) and to each key (at its token index)."""
     kv_len = K.shape[0]
     s0 = window_start(kv_len, window_left)
     qf, Kf, Vf = _request_f64(q_i, K[s0:], V[s0:], q_dtype, kv_dtype,
                               q_scale, k_scale, v_scale)
+    if rope is not None:
+        theta, scale = rope
+        qf = rope_rotate(qf[:, None, :], [kv_len - 1], theta, scale)[:, 0, :]
+        Kf = rope_rotate(Kf.transpose(1, 0, 2), np.arange(s0, kv_len), theta,
+                         scale).transpose(1, 0, 2)
     bias = None
     if alibi:
         # the query sits at kv_len - 1; token t is (kv_len - 1 - t) behind it
@@ -240,7 +270,7 @@ def batch_decode(q, paged_kv_cache, layout: str, indptr, indices,
                  sm_scale: float, logits_soft_cap: float = 0.0,
                  window_left: int = -1, q_scale: float = 1.0,
                  k_scale: float = 1.0, v_scale: float = 1.0, requests=None,
-                 sinks=None, alibi: bool = False):
+                 sinks=None, alibi: bool = False, rope=None):
     """o [len(requests), num_qo_heads, head_dim] and lse, both fp64.
 
     ``q`` is [batch, num_qo_heads, head_dim] in its stored dtype;
@@ -258,7 +288,7 @@ def batch_decode(q, paged_kv_cache, layout: str, indptr, indices,
                               int(lens[i]), page_size)
         o[r], lse[r] = decode_request(q[i], K, V, q_dtype, kv_dtype, sm_scale,
                                       logits_soft_cap, window_left, q_scale,
-                                      k_scale, v_scale, sinks, alibi)
+                                      k_scale, v_scale, sinks, alibi, rope)
     return o, lse
 
 
@@ -352,7 +382,7 @@ def batch_decode_multi(q, paged_kv_cache, layout: str, indptr, indices,
                        logits_soft_cap: float = 0.0, window_left: int = -1,
                        q_scale: float = 1.0, k_scale: float = 1.0,
                        v_scale: float = 1.0, requests=None, sinks=None,
-                       alibi: bool = False):
+                       alibi: bool = False, rope=None):
     """Decode with q_len_per_req query tokens per request, fp64.
 
     ``q`` is [batch * q_len_per_req, num_qo_heads, head_dim] (request-major,
@@ -381,5 +411,5 @@ def batch_decode_multi(q, paged_kv_cache, layout: str, indptr, indices,
             o[r * Q + j], lse[r * Q + j] = decode_request(
                 q[i * Q + j], K[:pos + 1], V[:pos + 1], q_dtype, kv_dtype,
                 sm_scale, logits_soft_cap, window_left, q_scale, k_scale,
-                v_scale, sinks, alibi)
+                v_scale, sinks, alibi, rope)
     return o, lse

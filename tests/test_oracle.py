@@ -646,3 +646,54 @@ def test_alibi_matches_sdpa_with_a_distance_bias(Q, window):
         ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(bias),
                                              scale=0.3, enable_gqa=True)[0].numpy()
         assert np.max(np.abs(o[i * Q:(i + 1) * Q] - ref.transpose(1, 0, 2))) < 1e-12
+
+
+# ---------------------------------------------------------------- ROPE_LLAMA
+
+def test_rope_of_a_two_dim_head_is_a_plane_rotation():
+    # head_dim 2: one pair, frequency theta^0 = 1, angle = position / scale
+    x = np.array([[0.3, -1.2], [2.0, 0.5]])
+    for scale in (1.0, 4.0):
+        r = oracle.rope_rotate(x, [7, 130000], rope_scale=scale)
+        for row, pos in zip(range(2), (7, 130000)):
+            a = pos / scale
+            ref = [x[row, 0] * math.cos(a) - x[row, 1] * math.sin(a),
+                   x[row, 1] * math.cos(a) + x[row, 0] * math.sin(a)]
+            assert np.allclose(r[row], ref, atol=1e-12)
+
+
+def test_rope_dot_products_depend_on_position_differences_only():
+    rng = np.random.default_rng(9)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    base = oracle.rope_rotate(q[None], [1000])[0] @ oracle.rope_rotate(k[None], [990])[0]
+    for shift in (1, 17, 50000):
+        d = oracle.rope_rotate(q[None], [1000 + shift])[0] @ \
+            oracle.rope_rotate(k[None], [990 + shift])[0]
+        assert abs(d - base) < 1e-9
+    # rotations keep norms, and position 0 is the identity
+    assert np.allclose(np.linalg.norm(oracle.rope_rotate(q[None], [12345])), np.linalg.norm(q))
+    assert np.array_equal(oracle.rope_rotate(q[None], [0])[0], q)
+
+
+def test_rope_decode_matches_sdpa_on_rotated_inputs():
+    """Decode with ROPE_LLAMA = SDPA (fp64) over keys rotated at their token
+    positions by an independent rotation (complex multiplication), q rotated
+    at its query position."""
+    rng = np.random.default_rng(10)
+    nkv, group, hd, L = 2, 2, 16, 37
+    theta, scale = 500.0, 2.0
+    K, V = rng.standard_normal((L, nkv, hd)), rng.standard_normal((L, nkv, hd))
+    q = rng.standard_normal((1, nkv * group, hd))
+    cache, indptr, indices, last = scatter_to_pages([K], [V], "NHD", 4, 12, rng)
+    o, _ = oracle.batch_decode(q, cache, "NHD", indptr, indices, last, 4, "f64", "f64",
+                               0.25, rope=(theta, scale))
+
+    def rot(x, pos):   # pairs as complex numbers times e^{i angle}
+        half = hd // 2
+        w = np.exp(1j * pos / scale * theta ** (-2.0 * np.arange(half) / hd))
+        z = (x[..., :half] + 1j * x[..., half:]) * w
+        return np.concatenate([z.real, z.imag], axis=-1)
+    Kr = np.stack([rot(K[t], t) for t in range(L)])
+    qr = rot(q[0], L - 1)
+    ref = sdpa_decode(qr, Kr, V, 0.25)
+    assert np.max(np.abs(o[0] - ref)) < 1e-12
