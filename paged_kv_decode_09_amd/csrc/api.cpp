@@ -47,6 +47,12 @@ struct pkd_plan {
     return ((size_t)host.info.num_workgroups * 2 * 4 + 63) & ~(size_t)63;   // two per workgroup
   }
   size_t item_capacity() const { return graph ? (size_t)cap_items : host.items.size(); }
+  // ROPE_LLAMA: [head_dim/2][2] rotary frequencies (revolutions per token as
+  // an unevaluated float sum hi + lo)
+  bool rope() const { return host.params.pos_encoding_mode == PKD_POS_ROPE_LLAMA; }
+  size_t rope_bytes() const {
+    return rope() ? ((size_t)host.params.head_dim / 2 * 8 + 63) & ~(size_t)63 : 0;
+  }
   int32_t ws_partials() const { return graph ? cap_partials : host.info.num_partials; }
   int32_t* d_counters() const { return reinterpret_cast<int32_t*>(dev); }
   int32_t* d_reserve() const {
@@ -56,10 +62,15 @@ struct pkd_plan {
     return reinterpret_cast<int32_t*>(reinterpret_cast<char*>(dev) + kCounterBytes +
                                       reserve_bytes());
   }
+  size_t rope_offset() const { return kCounterBytes + reserve_bytes() + merge_counter_bytes(); }
+  const float* d_rope() const {
+    return rope() ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(dev) +
+                                                   rope_offset())
+                  : nullptr;
+  }
   const pkd_work_item* d_items() const {
     return reinterpret_cast<const pkd_work_item*>(reinterpret_cast<const char*>(dev) +
-                                                  kCounterBytes + reserve_bytes() +
-                                                  merge_counter_bytes());
+                                                  rope_offset() + rope_bytes());
   }
 };
 
@@ -83,7 +94,7 @@ void free_plan(pkd_plan* p) {
 size_t plan_bytes(const pkd_plan& p) {
   if (p.item_capacity() == 0) return 0;
   return pkd_plan::kCounterBytes + p.reserve_bytes() + p.merge_counter_bytes() +
-         p.item_capacity() * sizeof(pkd_work_item);
+         p.rope_bytes() + p.item_capacity() * sizeof(pkd_work_item);
 }
 
 // Fills the staging copy from the host plan and uploads it on `stream`
@@ -105,7 +116,19 @@ pkd_status upload(pkd_plan* p, void* stream) {
   std::memset(s + pkd_plan::kCounterBytes, 0xFF, p->reserve_bytes());
   const size_t zeros = pkd_plan::kCounterBytes + p->reserve_bytes();
   std::memset(s + zeros, 0, p->merge_counter_bytes());
-  std::memcpy(s + zeros + p->merge_counter_bytes(), p->host.items.data(),
+  if (p->rope()) {
+    // pair i turns by position / rope_scale * rope_theta^(-2i/head_dim)
+    // radians per token; in revolutions, as a hi + lo float pair
+    const pkd_plan_params& pp = p->host.params;
+    float* f = reinterpret_cast<float*>(s + p->rope_offset());
+    for (int i = 0; i < pp.head_dim / 2; ++i) {
+      const double rev = std::pow((double)pp.rope_theta, -2.0 * i / pp.head_dim) /
+                         ((double)pp.rope_scale * 2.0 * 3.14159265358979323846);
+      f[2 * i] = (float)rev;
+      f[2 * i + 1] = (float)(rev - (double)f[2 * i]);
+    }
+  }
+  std::memcpy(s + p->rope_offset() + p->rope_bytes(), p->host.items.data(),
               p->host.items.size() * sizeof(pkd_work_item));
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   e = hipMemcpyAsync(p->dev, p->staging, bytes, hipMemcpyHostToDevice, hs);
@@ -436,6 +459,7 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
   a.cols = a.group * Q;
   a.window_left = p.window_left;
   a.alibi = p.pos_encoding_mode == PKD_POS_ALIBI;
+  a.rope_freq = plan->d_rope();
   int lg = 0;
   while ((1 << lg) < p.page_size) ++lg;
   a.log2_page = lg;

@@ -65,6 +65,20 @@ __device__ __forceinline__ float tanh_from_exp(float y) {
   return 1.0f - 2.0f * __builtin_amdgcn_rcpf(e + 1.0f);
 }
 
+// cos and sin of the rotary angle of position t for a frequency given in
+// revolutions per token as an unevaluated sum f.x + f.y: t * f.x is split
+// into its rounded product and exact residual (an fma), the whole
+// revolutions are dropped exactly, and the hardware sine and cosine (which
+// take revolutions) see an argument in [-1, 2].
+__device__ __forceinline__ void rope_cos_sin(int t, f32x2 f, float& c, float& sn) {
+  const float tf = (float)t;                          // exact below 2^24
+  const float p = tf * f[0];
+  const float e = __builtin_fmaf(tf, f[0], -p);
+  const float r = (p - __builtin_floorf(p)) + __builtin_fmaf(tf, f[1], e);
+  c = __builtin_amdgcn_cosf(r);
+  sn = __builtin_amdgcn_sinf(r);
+}
+
 // Operand type of the MFMA: the q dtype (fp8 K/V are converted to it).
 template <bool BF16>
 struct Op;
@@ -72,6 +86,7 @@ struct Op;
 template <>
 struct Op<false> {
   using v8 = f16x8;
+  using et = _Float16;
   __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
@@ -84,6 +99,7 @@ struct Op<false> {
 template <>
 struct Op<true> {
   using v8 = bf16x8;
+  using et = __bf16;
   __device__ static f32x4 mfma(v8 a, v8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -351,7 +367,7 @@ struct Win {
   int64_t head_off;
 };
 
-template <int HD, bool QBF16, bool KV8, bool CAP>
+template <int HD, bool QBF16, bool KV8, bool CAP, bool ROPE>
 __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void decode_kernel(DecodeArgs args) {
   DecodeArgs a = args;
   if (args.plan_header != nullptr) {
@@ -372,7 +388,14 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   __shared__ int s_last;
   __shared__ unsigned long long s_steal;
   __shared__ int s_drop;
+  // rotary frequencies [HD/2] (revolutions per token, hi + lo), ROPE only
+  __shared__ f32x2 s_rope[ROPE ? HD / 2 : 1];
 
+  if constexpr (ROPE) {
+    for (int i = threadIdx.x; i < HD / 2; i += kWaves * 64)
+      s_rope[i] = reinterpret_cast<const f32x2*>(a.rope_freq)[i];
+    lds_barrier();
+  }
   const int lane = threadIdx.x & 63;
   // wave-uniform (an SGPR), so that the step loop branches on scalars
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -460,26 +483,64 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   // logit's bits unchanged.
   float col_slope = 0.0f;
 
+  // ROPE_LLAMA: operand pieces j and j + kQkMfma/2 of a lane hold the two
+  // halves (d, d + HD/2) of the same rotary pairs, so each lane turns its
+  // own elements. Element e of piece j is hd index qk_hd(j, g) + e.
+  constexpr int kHalf = G_::kQkMfma / 2;
+  auto rope_pair = [&](v8& lo_op, v8& hi_op, int j, int pos) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float c, sn;
+      rope_cos_sin(pos, s_rope[qk_hd<KV8>(j, g) + e], c, sn);
+      const float lo = (float)lo_op[e], hi = (float)hi_op[e];
+      lo_op[e] = (typename O::et)(lo * c - hi * sn);
+      hi_op[e] = (typename O::et)(hi * c + lo * sn);
+    }
+  };
+  // the K operand of piece j of tile `tile`
+  auto k_operand = [&](const StepRegs<G_::kPieces>& st, int tile, int j) {
+    if constexpr (KV8) {
+      const u32x4 w = st.k[tile][j >> 1];
+      return (j & 1) ? e4m3x8<QBF16>(w[2], w[3]) : e4m3x8<QBF16>(w[0], w[1]);
+    } else {
+      return __builtin_bit_cast(v8, st.k[tile][j]);
+    }
+  };
+  bool q_turned = false;   // this unit's q has been rotated (ROPE only)
+
   // Attend step s of window W whose K/V rows are in st. A step wholly past
   // the window (the padding step of an odd count) changes nothing.
   auto consume = [&](const Win& W, int s, const StepRegs<G_::kPieces>& st) {
     const int t0 = W.base + s * kStepTokens;
     if (t0 > W.whi) return;
+    if constexpr (ROPE) {
+      // q at its query position, once per unit (its loads have landed by
+      // the unit's first step)
+      if (!q_turned) {
+#pragma unroll
+        for (int j = 0; j < kHalf; ++j) rope_pair(bq[j], bq[j + kHalf], j, col_hi);
+        q_turned = true;
+      }
+    }
     // ---- logits: S[tile] rows = tokens, columns = heads
     f32x4 sc[2];
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
       f32x4 acc_s = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (ROPE) {
+        // each key at the token index its row was loaded from, a rotary
+        // pair of pieces at a time
+        const int tok = token(W, s, tile ? tau1 : tau0);
 #pragma unroll
-      for (int j = 0; j < G_::kQkMfma; ++j) {
-        v8 kop;
-        if constexpr (KV8) {
-          const u32x4 w = st.k[tile][j >> 1];
-          kop = (j & 1) ? e4m3x8<QBF16>(w[2], w[3]) : e4m3x8<QBF16>(w[0], w[1]);
-        } else {
-          kop = __builtin_bit_cast(v8, st.k[tile][j]);
+        for (int j = 0; j < kHalf; ++j) {
+          v8 lo = k_operand(st, tile, j), hi = k_operand(st, tile, j + kHalf);
+          rope_pair(lo, hi, j, tok);
+          acc_s = O::mfma(lo, bq[j], acc_s);
+          acc_s = O::mfma(hi, bq[j + kHalf], acc_s);
         }
-        acc_s = O::mfma(kop, bq[j], acc_s);
+      } else {
+#pragma unroll
+        for (int j = 0; j < G_::kQkMfma; ++j) acc_s = O::mfma(k_operand(st, tile, j), bq[j], acc_s);
       }
       sc[tile] = acc_s;
     }
@@ -682,6 +743,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
 
       m_run = -INFINITY;
       d_run = 0.0f;
+      q_turned = false;
       col_hi = cu.qpos + col_tok;
       col_lo = a.window_left < 0 ? 0 : col_hi - a.window_left;
       if (a.alibi) {
@@ -996,28 +1058,33 @@ __global__ __launch_bounds__(kMergeRowsPerBlock * 64) void merge_kernel(MergeArg
     a.s_out[row] = M == -INFINITY ? -INFINITY : (M + __builtin_amdgcn_logf(den)) * kLn2;
 }
 
-// The kernel instance for (head_dim, q type, KV type, soft cap).
+// The kernel instance for (head_dim, q type, KV type, soft cap, RoPE).
 using DecodeFn = void (*)(DecodeArgs);
 
-template <bool QBF16, bool KV8, bool CAP>
+template <bool QBF16, bool KV8, bool CAP, bool ROPE>
 DecodeFn pick_hd(int hd) {
   switch (hd) {
-    case 64: return decode_kernel<64, QBF16, KV8, CAP>;
-    case 128: return decode_kernel<128, QBF16, KV8, CAP>;
-    default: return decode_kernel<256, QBF16, KV8, CAP>;
+    case 64: return decode_kernel<64, QBF16, KV8, CAP, ROPE>;
+    case 128: return decode_kernel<128, QBF16, KV8, CAP, ROPE>;
+    default: return decode_kernel<256, QBF16, KV8, CAP, ROPE>;
   }
 }
 
-DecodeFn pick_kernel(const pkd_plan_params& p) {
+template <bool ROPE>
+DecodeFn pick_types(const pkd_plan_params& p) {
   const bool cap = p.logits_soft_cap > 0.0f;
   const bool qbf = p.q_dtype == PKD_BF16;
   const bool kv8 = p.kv_dtype == PKD_E4M3;
   if (qbf) {
-    if (kv8) return cap ? pick_hd<true, true, true>(p.head_dim) : pick_hd<true, true, false>(p.head_dim);
-    return cap ? pick_hd<true, false, true>(p.head_dim) : pick_hd<true, false, false>(p.head_dim);
+    if (kv8) return cap ? pick_hd<true, true, true, ROPE>(p.head_dim) : pick_hd<true, true, false, ROPE>(p.head_dim);
+    return cap ? pick_hd<true, false, true, ROPE>(p.head_dim) : pick_hd<true, false, false, ROPE>(p.head_dim);
   }
-  if (kv8) return cap ? pick_hd<false, true, true>(p.head_dim) : pick_hd<false, true, false>(p.head_dim);
-  return cap ? pick_hd<false, false, true>(p.head_dim) : pick_hd<false, false, false>(p.head_dim);
+  if (kv8) return cap ? pick_hd<false, true, true, ROPE>(p.head_dim) : pick_hd<false, true, false, ROPE>(p.head_dim);
+  return cap ? pick_hd<false, false, true, ROPE>(p.head_dim) : pick_hd<false, false, false, ROPE>(p.head_dim);
+}
+
+DecodeFn pick_kernel(const pkd_plan_params& p) {
+  return p.pos_encoding_mode == PKD_POS_ROPE_LLAMA ? pick_types<true>(p) : pick_types<false>(p);
 }
 
 }  // namespace

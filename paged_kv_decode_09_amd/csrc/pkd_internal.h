@@ -148,6 +148,9 @@ struct DecodeArgs {
   int32_t cols;         // G * Q <= kMaxGroup: query rows of a unit
   int32_t window_left;  // -1, or the left window of each query token
   int32_t alibi;        // nonzero: ALiBi bias on the logits
+  // ROPE_LLAMA: [head_dim/2][2] rotary frequencies in revolutions per token
+  // (hi, lo), else NULL
+  const float* rope_freq;
   int32_t log2_page;
   int32_t o_bf16;       // output dtype: 0 = f16, 1 = bf16
   float logit_scale;    // sm_scale*q_scale*k_scale (times log2 e if no cap)

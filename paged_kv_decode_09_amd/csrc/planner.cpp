@@ -89,9 +89,18 @@ pkd_status check_params(const pkd_plan_params& p) {
     return fail(PKD_EUNSUPPORTED,
                 fmt("group size %d (num_qo_heads/num_kv_heads) exceeds %d",
                     group, kMaxGroup));
-  if (p.pos_encoding_mode == PKD_POS_ROPE_LLAMA)
-    return fail(PKD_EUNSUPPORTED, "pos_encoding_mode ROPE_LLAMA is not built (NONE and ALIBI are)");
-  if (p.pos_encoding_mode != PKD_POS_NONE && p.pos_encoding_mode != PKD_POS_ALIBI)
+  if (p.pos_encoding_mode == PKD_POS_ROPE_LLAMA) {
+    if (!(p.rope_scale > 0.0f) || !std::isfinite(p.rope_scale) || !(p.rope_theta > 0.0f) ||
+        !std::isfinite(p.rope_theta))
+      return fail(PKD_EINVAL, fmt("rope_scale %g and rope_theta %g must be positive and finite",
+                                  p.rope_scale, p.rope_theta));
+    // each lane rotates pairs (d, d + head_dim/2) it holds itself; with
+    // head_dim 64 and E4M3 keys the two halves sit in different lanes
+    if (p.head_dim == 64 && p.kv_dtype == PKD_E4M3)
+      return fail(PKD_EUNSUPPORTED, "ROPE_LLAMA with head_dim 64 and E4M3 keys is not built");
+  }
+  if (p.pos_encoding_mode != PKD_POS_NONE && p.pos_encoding_mode != PKD_POS_ALIBI &&
+      p.pos_encoding_mode != PKD_POS_ROPE_LLAMA)
     return fail(PKD_EINVAL, fmt("pos_encoding_mode %d is not NONE (0), ROPE_LLAMA (1) or ALIBI (2)",
                                 p.pos_encoding_mode));
   if (p.q_len_per_req < 0)
@@ -206,6 +215,9 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
       return fail(PKD_EUNSUPPORTED,
                   fmt("request %d has kv_len %lld > %d", i, (long long)L,
                       INT32_MAX / 2));
+    if (p.pos_encoding_mode == PKD_POS_ROPE_LLAMA && L > (1 << 24))
+      return fail(PKD_EUNSUPPORTED, fmt("request %d has kv_len %lld > 2^24, beyond the exact "
+                                        "positions of the rotary angles", i, (long long)L));
     if (L < Q)
       return fail(PKD_EINVAL, fmt("request %d has kv_len %lld < q_len_per_req %d: its "
                                   "first query token would have no position",
