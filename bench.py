@@ -92,13 +92,19 @@ def run_cpu_baseline(w, case, budget_s=10.0):
     done, elapsed, nbytes, tokens = [], 0.0, 0, 0
     kw = dict(logits_soft_cap=w.logits_soft_cap, window_left=w.window_left,
               k_scale=w.k_scale, v_scale=w.v_scale)
+    rope = (w.rope_theta, w.rope_scale) \
+        if w.pos_encoding_mode == "ROPE_LLAMA" else None
+    alibi = w.pos_encoding_mode == "ALIBI"
+    if rope or alibi:
+        # only the one-token / multi-token oracle entry takes these
+        kw.update(rope=rope, alibi=alibi)
     Q = w.q_len_per_req
     for i in order:
         pool, indptr, indices, last = _sub_pool(case, [i])
         qn = wl.raw_numpy(case.q[i * Q:(i + 1) * Q], w.q_dtype)
         pn = wl.raw_numpy(pool, w.kv_dtype)
         t = time.perf_counter()
-        if Q > 1:
+        if Q > 1 or "rope" in kw:
             oracle.batch_decode_multi(qn, pn, w.layout, indptr, indices, last,
                                       w.page_size, Q, w.q_dtype, w.kv_dtype,
                                       w.sm_scale, **kw)
@@ -180,7 +186,8 @@ def main():
         window_left=w.window_left, logits_soft_cap=w.logits_soft_cap or None,
         q_data_type=w.q_dtype, kv_data_type=w.kv_dtype, o_data_type=w.o_dtype,
         sm_scale=w.sm_scale, fixed_split_size=w.fixed_split_size or None,
-        q_len_per_req=w.q_len_per_req)
+        q_len_per_req=w.q_len_per_req, pos_encoding_mode=w.pos_encoding_mode,
+        rope_theta=w.rope_theta, rope_scale=w.rope_scale)
     info = plan.info
     rows = w.batch * w.q_len_per_req
     o = torch.empty((rows, w.num_qo_heads, w.head_dim),
@@ -282,6 +289,7 @@ def main():
             "window_left": w.window_left,
             "fixed_split_size": w.fixed_split_size,
             "q_len_per_req": w.q_len_per_req,
+            "pos_encoding_mode": w.pos_encoding_mode,
             "split_pages_used": info.split_pages,
             "work_items": info.num_items,
             "attended_tokens": int(info.attended_tokens),

@@ -52,6 +52,9 @@ class Workload:
     k_scale: float = 1.0
     v_scale: float = 1.0
     q_len_per_req: int = 1    # query tokens per request (q has batch * this rows)
+    pos_encoding_mode: str = "NONE"   # NONE | ALIBI | ROPE_LLAMA
+    rope_theta: float = 1e4
+    rope_scale: float = 1.0
     note: str = field(default="", compare=False)
 
     @property
@@ -88,6 +91,11 @@ WORKLOADS = {
         ("uniform", 512, 4096), pages="perm_pool", pool_pages=20000,
         q_len_per_req=4,
         note="the serving batch with 4 query tokens per request (causal)"),
+    "serving_rope": Workload(
+        "serving_rope", 2, 64, 32, 8, 128, 16, "bf16", "bf16", "bf16", "HND",
+        ("uniform", 512, 4096), pages="perm_pool", pool_pages=20000,
+        pos_encoding_mode="ROPE_LLAMA",
+        note="the serving batch with Llama-style rotary embedding in the kernel"),
 }
 
 

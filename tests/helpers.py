@@ -22,7 +22,9 @@ def plan_for(w, case, **overrides):
               q_data_type=w.q_dtype, kv_data_type=w.kv_dtype,
               o_data_type=w.o_dtype, sm_scale=w.sm_scale,
               fixed_split_size=w.fixed_split_size or None,
-              q_len_per_req=w.q_len_per_req)
+              q_len_per_req=w.q_len_per_req,
+              pos_encoding_mode=w.pos_encoding_mode, rope_theta=w.rope_theta,
+              rope_scale=w.rope_scale)
     kw.update(overrides)
     indices = torch.from_numpy(case.pt.indices).to("cuda")
     return pkd.PagedDecodePlan(case.pt.indptr, indices, case.pt.last_page_len,
