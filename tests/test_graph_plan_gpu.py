@@ -38,8 +38,10 @@ def tables(w, seeds):
     return out
 
 
-@pytest.mark.parametrize("split,Q", [(None, 1), (2, 1), ("off", 1), (None, 2)])
-def test_graph_replays_follow_each_new_plan(split, Q):
+@pytest.mark.parametrize("split,Q,pos", [(None, 1, "NONE"), (2, 1, "NONE"), ("off", 1, "NONE"),
+                                         (None, 2, "NONE"), (None, 1, "ROPE_LLAMA"),
+                                         (2, 2, "ALIBI")])
+def test_graph_replays_follow_each_new_plan(split, Q, pos):
     w = wl.small_workload(seed=79, batch=6, num_qo_heads=8, num_kv_heads=2, head_dim=128,
                           q_dtype="bf16", kv_dtype="bf16", o_dtype="bf16", layout="HND",
                           q_len_per_req=Q, pages="perm_pool", pool_pages=POOL)
@@ -47,7 +49,8 @@ def test_graph_replays_follow_each_new_plan(split, Q):
     pool = wl.make_pool(w, POOL, "cuda")
     kw = dict(q_data_type=torch.bfloat16, q_len_per_req=Q,
               fixed_split_size=split if isinstance(split, int) else None,
-              disable_split_kv=split == "off")
+              disable_split_kv=split == "off", pos_encoding_mode=pos)
+    sinks = torch.linspace(-2.0, 3.0, 8, device="cuda") if pos != "NONE" else None
     dev = "cuda"
     wrapper = pkd.CUDAGraphBatchDecodeWithPagedKVCacheWrapper(
         torch.empty(64 << 20, dtype=torch.uint8, device=dev),
@@ -63,11 +66,11 @@ def test_graph_replays_follow_each_new_plan(split, Q):
     wrapper.plan(pt0.indptr, torch.from_numpy(pt0.indices).to(dev), pt0.last_page_len,
                  8, 2, 128, 16, **kw)
     q_static.copy_(q0)
-    wrapper.run(q_static, pool, out=o_static, lse=l_static)   # warm-up, eager
+    wrapper.run(q_static, pool, out=o_static, lse=l_static, sinks=sinks)   # warm-up, eager
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        wrapper.run(q_static, pool, out=o_static, lse=l_static)
+        wrapper.run(q_static, pool, out=o_static, lse=l_static, sinks=sinks)
     torch.cuda.synchronize()
     for k, (pt, q) in enumerate(cases + cases[:1]):
         say("page table", k, "pages", int(pt.indptr[-1]))
@@ -81,9 +84,11 @@ def test_graph_replays_follow_each_new_plan(split, Q):
         idx = torch.from_numpy(pt.indices).to(dev)
         plain = pkd.PagedDecodePlan(pt.indptr, idx, pt.last_page_len, 8, 2, 128, 16,
                                     kv_layout="HND", **kw)
-        o_ref, l_ref = plain.run(q, pool, return_lse=True)
+        o_ref, l_ref = plain.run(q, pool, return_lse=True, sinks=sinks)
         torch.cuda.synchronize()
         assert torch.equal(o_static, o_ref) and torch.equal(l_static, l_ref), k
+    if pos != "NONE":
+        return   # (those modes have their own oracle tests)
     # and against the oracle, for the last table
     case = wl.Case(replace(w, batch=6), pt, q, pool)
     ref_o, ref_l = oracle_for(case.w, case)
