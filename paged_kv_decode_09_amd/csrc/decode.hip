@@ -194,8 +194,10 @@ struct Geo {
   // LDS row pitch of the V copy; the pad staggers rows across banks.
   static constexpr int kVPitch = kRowBytes + (KV8 ? 16 : 32);
   static constexpr int kVBytes = kStepTokens * kVPitch;
+  // K rows are staged in a region of their own, after the V rows
+  static constexpr int kStageBytes = 2 * kVBytes;
   static constexpr int kMergeBytes = kMaxGroup * HD * 4;
-  static constexpr int kWaveLds = kVBytes > kMergeBytes ? kVBytes : kMergeBytes;
+  static constexpr int kWaveLds = kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes;
 };
 
 // Page ids of the item are staged in LDS, a window at a time, so that the
@@ -434,25 +436,52 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   auto token = [&](const Win& W, int s, int tau) {
     return min(max(W.base + s * kStepTokens + tau, W.wlo), W.whi);
   };
-  // Issue the K/V loads of the rows of tokens c0, c1 (in pages pg0, pg1).
-  auto issue_rows = [&](const Win& W, int c0, int c1, int pg0, int pg1, StepRegs<G_::kPieces>& st) {
-    const int64_t r0 = ((int64_t)pg0 * a.page_stride + (int64_t)(c0 & page_mask) * a.slot_stride + W.head_off) * G_::kKvBytes;
-    const int64_t r1 = ((int64_t)pg1 * a.page_stride + (int64_t)(c1 & page_mask) * a.slot_stride + W.head_off) * G_::kKvBytes;
+  // Whole-line loads. Lane l loads 16-byte chunk (l % kLr) of step row
+  // l / kLr + kRowsPer * b: one load instruction covers kLr * 16 contiguous
+  // bytes of each of its rows, whole 128-byte lines when a row holds one.
+  // (Loads of 64 bytes from each of 16 rows, the layout the MFMA operand
+  // wants, stream about 15 % slower from HBM.) The rows reach the MFMA
+  // layout through this wave's LDS copy (consume).
+  constexpr int kChunks = G_::kRowBytes / 16;
+  constexpr int kLr = kChunks < 8 ? kChunks : 8;
+  constexpr int kRowsPer = 64 / kLr;
+  constexpr int kRowBlocks = kStepTokens / kRowsPer;   // rows per lane and step
+  constexpr int kChunkBlocks = kChunks / kLr;
+  constexpr int kNP = G_::kPieces;
+  static_assert(kRowBlocks * kChunkBlocks == 2 * kNP, "one register per load");
+  const int lrow = lane / kLr, lchunk = lane % kLr;
+  // Issue the K/V loads of this lane's rows: tokens c[b] in pages pg[b].
+  auto issue_rows = [&](const Win& W, const int (&c)[kRowBlocks], const int (&pg)[kRowBlocks],
+                        StepRegs<kNP>& st) {
+    int64_t rb[kRowBlocks];
 #pragma unroll
-    for (int p = 0; p < G_::kPieces; ++p) {
-      st.k[0][p] = *reinterpret_cast<const u32x4*>(kbase + r0 + 64 * p + 16 * g);
-      st.k[1][p] = *reinterpret_cast<const u32x4*>(kbase + r1 + 64 * p + 16 * g);
-    }
+    for (int b = 0; b < kRowBlocks; ++b)
+      rb[b] = ((int64_t)pg[b] * a.page_stride + (int64_t)(c[b] & page_mask) * a.slot_stride +
+               W.head_off) * G_::kKvBytes;
 #pragma unroll
-    for (int p = 0; p < G_::kPieces; ++p) {
-      st.v[0][p] = *reinterpret_cast<const u32x4*>(vbase + r0 + 64 * p + 16 * g);
-      st.v[1][p] = *reinterpret_cast<const u32x4*>(vbase + r1 + 64 * p + 16 * g);
-    }
+    for (int q = 0; q < kChunkBlocks; ++q)
+#pragma unroll
+      for (int b = 0; b < kRowBlocks; ++b) {
+        const int i = q * kRowBlocks + b;
+        st.k[i / kNP][i % kNP] = *reinterpret_cast<const u32x4*>(kbase + rb[b] + 16 * (q * kLr + lchunk));
+      }
+#pragma unroll
+    for (int q = 0; q < kChunkBlocks; ++q)
+#pragma unroll
+      for (int b = 0; b < kRowBlocks; ++b) {
+        const int i = q * kRowBlocks + b;
+        st.v[i / kNP][i % kNP] = *reinterpret_cast<const u32x4*>(vbase + rb[b] + 16 * (q * kLr + lchunk));
+      }
   };
   // Issue the K/V loads of step s of window W (page ids from its LDS window).
-  auto issue = [&](const Win& W, int s, StepRegs<G_::kPieces>& st) {
-    const int c0 = token(W, s, tau0), c1 = token(W, s, tau1);
-    issue_rows(W, c0, c1, W.sp[(c0 >> lp) - W.wpage0], W.sp[(c1 >> lp) - W.wpage0], st);
+  auto issue = [&](const Win& W, int s, StepRegs<kNP>& st) {
+    int c[kRowBlocks], pg[kRowBlocks];
+#pragma unroll
+    for (int b = 0; b < kRowBlocks; ++b) {
+      c[b] = token(W, s, lrow + kRowsPer * b);
+      pg[b] = W.sp[(c[b] >> lp) - W.wpage0];
+    }
+    issue_rows(W, c, pg, st);
   };
 
   // q operand: column n is query row n of the unit (query token n / G, q
@@ -497,22 +526,43 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
       hi_op[e] = (typename O::et)(hi * c + lo * sn);
     }
   };
-  // the K operand of piece j of tile `tile`
-  auto k_operand = [&](const StepRegs<G_::kPieces>& st, int tile, int j) {
+  // the K operand of piece j of tile `tile` (kr: K in the MFMA layout)
+  auto k_operand = [&](const u32x4 (&kr)[2][kNP], int tile, int j) {
     if constexpr (KV8) {
-      const u32x4 w = st.k[tile][j >> 1];
+      const u32x4 w = kr[tile][j >> 1];
       return (j & 1) ? e4m3x8<QBF16>(w[2], w[3]) : e4m3x8<QBF16>(w[0], w[1]);
     } else {
-      return __builtin_bit_cast(v8, st.k[tile][j]);
+      return __builtin_bit_cast(v8, kr[tile][j]);
     }
   };
   bool q_turned = false;   // this unit's q has been rotated (ROPE only)
 
   // Attend step s of window W whose K/V rows are in st. A step wholly past
   // the window (the padding step of an odd count) changes nothing.
-  auto consume = [&](const Win& W, int s, const StepRegs<G_::kPieces>& st) {
+  auto consume = [&](const Win& W, int s, const StepRegs<kNP>& st) {
     const int t0 = W.base + s * kStepTokens;
     if (t0 > W.whi) return;
+    // ---- the step's K and V rows to this wave's LDS copies (row = token
+    // within the step) as loaded; K read back in the MFMA layout (lane
+    // (n, g) of tile t: 64-byte piece p of row tau_t from byte 16 g). A
+    // wave's LDS accesses run in order, so the previous step's reads are
+    // done before these writes land.
+    char* kl = vl + G_::kVBytes;
+#pragma unroll
+    for (int q = 0; q < kChunkBlocks; ++q)
+#pragma unroll
+      for (int b = 0; b < kRowBlocks; ++b) {
+        const int i = q * kRowBlocks + b;
+        const int off = (lrow + kRowsPer * b) * G_::kVPitch + 16 * (q * kLr + lchunk);
+        *reinterpret_cast<u32x4*>(kl + off) = st.k[i / kNP][i % kNP];
+        *reinterpret_cast<u32x4*>(vl + off) = st.v[i / kNP][i % kNP];
+      }
+    u32x4 kr[2][kNP];
+#pragma unroll
+    for (int p = 0; p < kNP; ++p) {
+      kr[0][p] = *reinterpret_cast<const u32x4*>(kl + tau0 * G_::kVPitch + 64 * p + 16 * g);
+      kr[1][p] = *reinterpret_cast<const u32x4*>(kl + tau1 * G_::kVPitch + 64 * p + 16 * g);
+    }
     if constexpr (ROPE) {
       // q at its query position, once per unit (its loads have landed by
       // the unit's first step)
@@ -533,22 +583,16 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
         const int tok = token(W, s, tile ? tau1 : tau0);
 #pragma unroll
         for (int j = 0; j < kHalf; ++j) {
-          v8 lo = k_operand(st, tile, j), hi = k_operand(st, tile, j + kHalf);
+          v8 lo = k_operand(kr, tile, j), hi = k_operand(kr, tile, j + kHalf);
           rope_pair(lo, hi, j, tok);
           acc_s = O::mfma(lo, bq[j], acc_s);
           acc_s = O::mfma(hi, bq[j + kHalf], acc_s);
         }
       } else {
 #pragma unroll
-        for (int j = 0; j < G_::kQkMfma; ++j) acc_s = O::mfma(k_operand(st, tile, j), bq[j], acc_s);
+        for (int j = 0; j < G_::kQkMfma; ++j) acc_s = O::mfma(k_operand(kr, tile, j), bq[j], acc_s);
       }
       sc[tile] = acc_s;
-    }
-    // ---- V rows to this wave's LDS copy (row = token within the step)
-#pragma unroll
-    for (int p = 0; p < G_::kPieces; ++p) {
-      *reinterpret_cast<u32x4*>(vl + tau0 * G_::kVPitch + 64 * p + 16 * g) = st.v[0][p];
-      *reinterpret_cast<u32x4*>(vl + tau1 * G_::kVPitch + 64 * p + 16 * g) = st.v[1][p];
     }
     // ---- online softmax (base 2)
     const int lo = max(W.wlo, col_lo), hi = min(W.whi, col_hi);
@@ -644,7 +688,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   int nxt = cur + (int)gridDim.x;
   if (threadIdx.x == 0 && nxt < a.steal_limit)
     __hip_atomic_store(a.reserve + 2 * blockIdx.x + 1, nxt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  StepRegs<G_::kPieces> A, B;
+  StepRegs<kNP> A, B;
   Unit cu;
   unsigned itemv;
   unsigned claim = 0;     // what thread 0's claim of cur returned
@@ -729,7 +773,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
       // pages of this wave's first step of nxt (for the hand-over issue)
       Unit nu;
       Win Wn;
-      int nwpages, pgn, hpg0, hpg1;
+      int nwpages, pgn, hpg[kRowBlocks];
       const int32_t* npidx;
       auto load_next = [&]() {
         nu = unit_from_lanes(itemv);
@@ -737,8 +781,8 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
         nwpages = (Wn.whi >> lp) - Wn.wpage0 + 1;
         npidx = a.indices + nu.page_base;
         pgn = npidx[Wn.wpage0 + min((int)threadIdx.x, nwpages - 1)];
-        hpg0 = npidx[token(Wn, wave, tau0) >> lp];
-        hpg1 = npidx[token(Wn, wave, tau1) >> lp];
+#pragma unroll
+        for (int b = 0; b < kRowBlocks; ++b) hpg[b] = npidx[token(Wn, wave, lrow + kRowsPer * b) >> lp];
       };
 
       m_run = -INFINITY;
@@ -848,12 +892,15 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
                                     : 0x80000000u;
           claim = (unsigned)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32((int)kClaimStep, res_rsrc,
                                                                            coff, 0, 0);
-          const int c0 = token(W, s0 + m2 * kWaves, tau0);
-          const int c1 = token(W, s0 + m2 * kWaves, tau1);
-          const int pg0 = W.sp[(c0 >> lp) - W.wpage0];
-          const int pg1 = W.sp[(c1 >> lp) - W.wpage0];
-          issue_rows(hand ? Wn : W, hand ? token(Wn, wave, tau0) : c0,
-                     hand ? token(Wn, wave, tau1) : c1, hand ? hpg0 : pg0, hand ? hpg1 : pg1, A);
+          int cc[kRowBlocks], pp[kRowBlocks];
+#pragma unroll
+          for (int b = 0; b < kRowBlocks; ++b) {
+            const int cw = token(W, s0 + m2 * kWaves, lrow + kRowsPer * b);
+            const int pw = W.sp[(cw >> lp) - W.wpage0];
+            cc[b] = hand ? token(Wn, wave, lrow + kRowsPer * b) : cw;
+            pp[b] = hand ? hpg[b] : pw;
+          }
+          issue_rows(hand ? Wn : W, cc, pp, A);
         }
         __builtin_amdgcn_sched_barrier(0);
         consume(W, s0 + (m2 - 1) * kWaves, B);
