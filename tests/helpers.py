@@ -76,6 +76,13 @@ def oracle_for(w, case, requests=None, split_pages=None, q=None):
             w.kv_dtype, w.sm_scale)
     kw = dict(logits_soft_cap=w.logits_soft_cap, window_left=w.window_left,
               k_scale=w.k_scale, v_scale=w.v_scale)
+    if w.pos_encoding_mode != "NONE":
+        assert not split_pages, "the split oracle has no positional encoding"
+        pos = dict(rope=(w.rope_theta, w.rope_scale)) if w.pos_encoding_mode == "ROPE_LLAMA" \
+            else dict(alibi=True)
+        return oracle.batch_decode_multi(qn, pn, w.layout, indptr, indices, last,
+                                         w.page_size, w.q_len_per_req, w.q_dtype,
+                                         w.kv_dtype, w.sm_scale, **kw, **pos)
     if w.q_len_per_req > 1:
         return oracle.batch_decode_multi(qn, pn, w.layout, indptr, indices, last,
                                          w.page_size, w.q_len_per_req, w.q_dtype,

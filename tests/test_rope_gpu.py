@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from paged_kv_decode_09_amd import workloads as wl
-from helpers import LSE_TOL, max_abs, o_tol, plan_for, sub_pool
+from helpers import LSE_TOL, max_abs, o_tol, oracle_for, plan_for, run_gpu, sub_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -79,3 +79,21 @@ def test_rope_at_long_positions(kv):
     say(w)
     case = wl.make_case(w, device="cuda")
     check_rope(w, case, 1e4, 1.0, 64)
+
+
+def test_serving_rope_full_size():
+    """The serving batch with RoPE at full size, in the launch configuration
+    of the bench, on sampled requests (the oracle computes them one by one)."""
+    w = wl.WORKLOADS["serving_rope"]
+    say(w.name)
+    case = wl.make_case(w, device="cuda")
+    o, lse, plan = run_gpu(w, case)
+    assert not torch.isnan(o).any() and not torch.isnan(lse).any()
+    L = case.pt.lengths
+    reqs = sorted({0, w.batch - 1, int(np.argmin(L)), int(np.argmax(L)), 21})
+    ref_o, ref_l = oracle_for(w, case, reqs)
+    idx = torch.tensor(reqs)
+    eo, el = max_abs(o[idx], ref_o), max_abs(lse[idx], ref_l)
+    say(w.name, "requests", reqs, "o max-abs", eo, "lse max-abs", el,
+        "items", plan.info.num_items)
+    assert eo <= o_tol(w) and el <= rope_lse_tol(w)
