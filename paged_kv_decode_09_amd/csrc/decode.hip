@@ -453,6 +453,8 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   // Issue the K/V loads of this lane's rows: tokens c[b] in pages pg[b].
   auto issue_rows = [&](const Win& W, const int (&c)[kRowBlocks], const int (&pg)[kRowBlocks],
                         StepRegs<kNP>& st) {
+    // K and V rows are read once per launch: non-temporal loads (each one a
+    // whole 128-byte line) keep them from displacing other lines in the caches
     int64_t rb[kRowBlocks];
 #pragma unroll
     for (int b = 0; b < kRowBlocks; ++b)
@@ -463,14 +465,16 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
 #pragma unroll
       for (int b = 0; b < kRowBlocks; ++b) {
         const int i = q * kRowBlocks + b;
-        st.k[i / kNP][i % kNP] = *reinterpret_cast<const u32x4*>(kbase + rb[b] + 16 * (q * kLr + lchunk));
+        st.k[i / kNP][i % kNP] =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + rb[b] + 16 * (q * kLr + lchunk)));
       }
 #pragma unroll
     for (int q = 0; q < kChunkBlocks; ++q)
 #pragma unroll
       for (int b = 0; b < kRowBlocks; ++b) {
         const int i = q * kRowBlocks + b;
-        st.v[i / kNP][i % kNP] = *reinterpret_cast<const u32x4*>(vbase + rb[b] + 16 * (q * kLr + lchunk));
+        st.v[i / kNP][i % kNP] =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + rb[b] + 16 * (q * kLr + lchunk)));
       }
   };
   // Issue the K/V loads of step s of window W (page ids from its LDS window).
