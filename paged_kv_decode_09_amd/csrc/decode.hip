@@ -390,12 +390,19 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
   __shared__ int s_last;
   __shared__ unsigned long long s_steal;
   __shared__ int s_drop;
-  // rotary frequencies [HD/2] (revolutions per token, hi + lo), ROPE only
+  // rotary frequencies [HD/2] (revolutions per token, hi + lo), and the
+  // cosine and sine of the angle of a 4-token advance; ROPE only
   __shared__ f32x2 s_rope[ROPE ? HD / 2 : 1];
+  __shared__ f32x2 s_rope4[ROPE ? HD / 2 : 1];
 
   if constexpr (ROPE) {
-    for (int i = threadIdx.x; i < HD / 2; i += kWaves * 64)
-      s_rope[i] = reinterpret_cast<const f32x2*>(a.rope_freq)[i];
+    for (int i = threadIdx.x; i < HD / 2; i += kWaves * 64) {
+      const f32x2 f = reinterpret_cast<const f32x2*>(a.rope_freq)[i];
+      float c, sn;
+      rope_cos_sin(4, f, c, sn);
+      s_rope[i] = f;
+      s_rope4[i] = (f32x2){c, sn};
+    }
     lds_barrier();
   }
   const int lane = threadIdx.x & 63;
@@ -578,25 +585,47 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
     }
     // ---- logits: S[tile] rows = tokens, columns = heads
     f32x4 sc[2];
+    if constexpr (ROPE) {
+      // each key at its token index t0 + tau, a rotary pair of pieces at a
+      // time. Rows outside the window hold a clamped token's key and are
+      // masked below, so the unclamped index serves every row. Tile 1's rows
+      // are 4 tokens after tile 0's: their angles follow from tile 0's by
+      // the angle-addition formulas.
+      const int tok = t0 + tau0;
+      sc[0] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      sc[1] = sc[0];
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      f32x4 acc_s = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (ROPE) {
-        // each key at the token index its row was loaded from, a rotary
-        // pair of pieces at a time
-        const int tok = token(W, s, tile ? tau1 : tau0);
+      for (int j = 0; j < kHalf; ++j) {
+        v8 lo0 = k_operand(kr, 0, j), hi0 = k_operand(kr, 0, j + kHalf);
+        v8 lo1 = k_operand(kr, 1, j), hi1 = k_operand(kr, 1, j + kHalf);
 #pragma unroll
-        for (int j = 0; j < kHalf; ++j) {
-          v8 lo = k_operand(kr, tile, j), hi = k_operand(kr, tile, j + kHalf);
-          rope_pair(lo, hi, j, tok);
-          acc_s = O::mfma(lo, bq[j], acc_s);
-          acc_s = O::mfma(hi, bq[j + kHalf], acc_s);
+        for (int e = 0; e < 8; ++e) {
+          const int d = qk_hd<KV8>(j, g) + e;
+          float c0, s0;
+          rope_cos_sin(tok, s_rope[d], c0, s0);
+          const f32x2 r4 = s_rope4[d];
+          const float c1 = c0 * r4[0] - s0 * r4[1], s1 = s0 * r4[0] + c0 * r4[1];
+          float l = (float)lo0[e], h = (float)hi0[e];
+          lo0[e] = (typename O::et)(l * c0 - h * s0);
+          hi0[e] = (typename O::et)(h * c0 + l * s0);
+          l = (float)lo1[e];
+          h = (float)hi1[e];
+          lo1[e] = (typename O::et)(l * c1 - h * s1);
+          hi1[e] = (typename O::et)(h * c1 + l * s1);
         }
-      } else {
+        sc[0] = O::mfma(lo0, bq[j], sc[0]);
+        sc[0] = O::mfma(hi0, bq[j + kHalf], sc[0]);
+        sc[1] = O::mfma(lo1, bq[j], sc[1]);
+        sc[1] = O::mfma(hi1, bq[j + kHalf], sc[1]);
+      }
+    } else {
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        f32x4 acc_s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < G_::kQkMfma; ++j) acc_s = O::mfma(k_operand(kr, tile, j), bq[j], acc_s);
+        sc[tile] = acc_s;
       }
-      sc[tile] = acc_s;
     }
     // ---- online softmax (base 2)
     const int lo = max(W.wlo, col_lo), hi = min(W.whi, col_hi);
