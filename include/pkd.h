@@ -99,10 +99,14 @@ typedef struct {
   int32_t disable_split_kv; /* nonzero: exactly one chunk per request       */
   int32_t q_len_per_req;    /* Q, query tokens per request; 0 means 1;
                                G*Q <= 16 and every L_i >= Q                 */
-  int32_t pos_encoding_mode; /* pkd_pos_encoding: NONE or ALIBI (ROPE_LLAMA
-                               is rejected with PKD_EUNSUPPORTED)           */
-  float rope_scale;         /* RoPE parameters of plan(); unused unless     */
-  float rope_theta;         /* pos_encoding_mode is ROPE_LLAMA              */
+  int32_t pos_encoding_mode; /* pkd_pos_encoding. ROPE_LLAMA turns q at its
+                               position L_i - Q + j and each key at its token
+                               index (pairs d, d + head_dim/2); it is
+                               PKD_EUNSUPPORTED with head_dim 64 and E4M3
+                               keys, and for kv lengths above 2^24         */
+  float rope_scale;         /* ROPE_LLAMA: angle = pos / rope_scale *       */
+  float rope_theta;         /* rope_theta^(-2d/head_dim); both positive and
+                               finite (else PKD_EINVAL), unused otherwise   */
 } pkd_plan_params;
 
 /* One unit of decode work: the tokens [token_begin, token_end) of one chunk of

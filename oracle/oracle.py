@@ -33,18 +33,18 @@ unless stated otherwise):
 * Output (run() returns): o [batch, num_qo_heads, head_dim] and, on request,
   lse [batch, num_qo_heads], the log-sum-exp of the final logits. Reading
   taken: natural logarithm.
-* Split-KV (plan() parameter fixed_split_size, "in pages"): the sequence is
+* Split-KV (plan() parameter fixed_split_size, a count of pages): the sequence is
   cut into chunks of that many pages; per-chunk states are combined by a
   log-sum-exp merge (the merge_states step named there).
-* Positional encoding ALIBI (plan() parameter pos_encoding_mode, "applied
-  inside the attention kernel"). Readings taken: the slopes of the ALiBi
+* Positional encoding ALIBI (plan() parameter pos_encoding_mode; the
+  encoding happens within the attention kernel). Readings taken: the slopes of the ALiBi
   paper over the num_qo_heads q heads (for n a power of two, head h gets
   2^(-8(h+1)/n); otherwise the n' = 2^floor(log2 n) slopes of that rule,
   then the odd powers of 2^(-4/n') for the remaining heads), and the bias
   slope * (t - query position) is added to the scaled logit before the soft
   cap.
-* Positional encoding ROPE_LLAMA (same parameter; rope_scale "used in RoPE
-  interpolation", default 1; rope_theta default 1e4). Readings taken: the
+* Positional encoding ROPE_LLAMA (same parameter; rope_scale, the RoPE
+  interpolation factor, default 1; rope_theta default 1e4). Readings taken: the
   Llama-style rotary embedding rotates each pair (x[i], x[i + head_dim/2]),
   i < head_dim/2, of q (at its query position) and of every key (at its
   token index) by the angle position / rope_scale * rope_theta^(-2i/head_dim);
