@@ -109,20 +109,24 @@ struct Op<true> {
   }
 };
 
-// Eight E4M3 codes (little-endian in two dwords) -> eight operand values.
-// v_cvt_pk_f32_fp8 decodes OCP E4M3 exactly; the values are exact in fp16 and
-// bf16 too, so the second conversion does not round.
+// Eight E4M3 codes (little-endian in two dwords) -> eight operand values,
+// two per instruction with gfx950's scaled packed conversion (scale 1). Every
+// OCP E4M3 value is exact in fp16 and bf16, so nothing rounds: the results
+// equal a decode to fp32 followed by a pack.
 template <bool BF16>
 __device__ __forceinline__ typename Op<BF16>::v8 e4m3x8(unsigned lo, unsigned hi) {
-  f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-  f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-  f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-  f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
   u32x4 r;
-  r[0] = Op<BF16>::pack(a[0], a[1]);
-  r[1] = Op<BF16>::pack(b[0], b[1]);
-  r[2] = Op<BF16>::pack(c[0], c[1]);
-  r[3] = Op<BF16>::pack(d[0], d[1]);
+  if constexpr (BF16) {
+    r[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    r[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    r[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    r[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+  } else {
+    r[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false));
+    r[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true));
+    r[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false));
+    r[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true));
+  }
   return __builtin_bit_cast(typename Op<BF16>::v8, r);
 }
 
