@@ -133,6 +133,41 @@ def test_needle_gather_is_bit_exact(layout, kv, page_size):
                 assert torch.equal(o[i], exp[i]), (i, pos[i], split)
 
 
+@pytest.mark.parametrize("qd", ["bf16", "f16"])
+@pytest.mark.parametrize("layout", ["NHD", "HND"])
+def test_every_e4m3_code_decodes_exactly(qd, layout):
+    """V rows that hold all 254 finite E4M3 codes (the two NaN codes replaced
+    by 0), picked by a needle logit, come back as their exact values times
+    v_scale in the output dtype: the kernel's fp8 conversion rounds nothing."""
+    w = wl.small_workload(seed=45, batch=2, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                          page_size=16, layout=layout, lengths=("fixed", [40, 300]),
+                          q_dtype=qd, kv_dtype="e4m3", o_dtype=qd, k_scale=1 / 64,
+                          v_scale=1 / 64)
+    say(w)
+    case = wl.make_case(w, device="cuda")
+    codes = torch.arange(256, dtype=torch.int32)
+    codes[(codes == 0x7F) | (codes == 0xFF)] = 0
+    codes = codes.to(torch.uint8).cuda()
+    pos = {0: 17, 1: 250}
+    pool, q = plant_needles(w, case, pos, 1000.0)
+    pt = case.pt
+    for i, j in pos.items():
+        page = int(pt.indices[pt.indptr[i] + j // w.page_size])
+        slot = j % w.page_size
+        row = codes[128 * i:128 * (i + 1)]
+        if layout == "NHD":
+            pool[page, 1, slot] = row
+        else:
+            pool[page, 1, :, slot] = row
+    for split in (None, 2):
+        plan = plan_for(w, case, fixed_split_size=split)
+        o = plan.run(q, pool, k_scale=w.k_scale, v_scale=w.v_scale)
+        torch.cuda.synchronize()
+        exp = expected_rows(w, case, pool, pos)
+        for i in pos:
+            assert torch.equal(o[i], exp[i]), (i, split)
+
+
 def test_window_zero_returns_last_row_bit_exactly():
     w = wl.small_workload(seed=43, batch=5, num_qo_heads=32, num_kv_heads=8, head_dim=128,
                           lengths=("fixed", [1, 2, 16, 17, 999]), window_left=0,
