@@ -2,20 +2,30 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+The default workload is the largest one that fits one GPU, gemma2_decode
+(256 requests, head_dim 256, soft cap 50, window 4096; 4.99 GB per call).
+
 One step is one pkd_run (one kernel launch: decode, with the merge of split
-requests fused in) over one batch whose inputs already sit in HBM; the plan is built once before timing,
-as plan() is amortised over layers and steps. Successive steps alternate
-between distinct K/V pools so that no step finds the previous step's data in
-the 256 MB Infinity Cache.
+requests fused in) over one batch whose inputs already sit in HBM; the plan
+is built once before timing, as plan() is amortised over layers and steps.
+Successive steps alternate between distinct K/V pools so that no step finds
+the previous step's data in the 256 MB Infinity Cache. The class example
+(worked_example) runs the page's layer loop instead: one step is a pass over
+32 layers, each with its own cache, q and output, and the figures are per
+call.
 
 Prints one JSON line. ``value`` is the achieved HBM bandwidth of the whole
 call: algorithmic bytes / wall time per call, with the K timed calls replayed
 from one HIP graph (the way a serving loop issues its decode steps; pkd_run
-allocates nothing and never synchronises, so it captures unchanged);
-``--eager`` times K host launches instead. Algorithmic bytes = K and V rows
-of the attended tokens (each read once per kv head) + q + o + fp32 lse + the
-page indices of the touched pages + indptr + last_page_len.
-``roofline`` is that kernel, timed with HIP events on the stream it runs on. ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample.
+allocates nothing and never synchronises, so it captures unchanged); the
+graph is replayed R times and the median replay is reported, with the
+fastest and slowest beside it. ``--eager`` times K host launches instead.
+Algorithmic bytes = K and V rows of the attended tokens (each read once per
+kv head) + q + o + fp32 lse + the page indices of the touched pages + indptr
++ last_page_len. ``roofline`` is that kernel, timed with HIP events on the
+stream it runs on. ``cpu_baseline`` times the fp64 CPU oracle on a bounded
+sample: the median of three runs over the same requests, and for the two
+small workloads also a run limited to one thread.
 """
 import argparse
 import hashlib
@@ -80,58 +90,83 @@ def _sub_pool(case, requests):
         pt.last_page_len[list(requests)].astype(np.int32)
 
 
-def run_cpu_baseline(w, case, budget_s=10.0):
+def _oracle_call(w, case, i):
+    """The oracle on request i alone (argument marshalling only)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()]
-                      or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
-    order = list(range(w.batch))
-    done, elapsed, nbytes, tokens = [], 0.0, 0, 0
     kw = dict(logits_soft_cap=w.logits_soft_cap, window_left=w.window_left,
               k_scale=w.k_scale, v_scale=w.v_scale)
-    rope = (w.rope_theta, w.rope_scale) \
-        if w.pos_encoding_mode == "ROPE_LLAMA" else None
-    alibi = w.pos_encoding_mode == "ALIBI"
-    if rope or alibi:
-        # only the one-token / multi-token oracle entry takes these
-        kw.update(rope=rope, alibi=alibi)
+    if w.pos_encoding_mode == "ROPE_LLAMA":
+        kw["rope"] = (w.rope_theta, w.rope_scale)
+    elif w.pos_encoding_mode == "ALIBI":
+        kw["alibi"] = True
     Q = w.q_len_per_req
-    for i in order:
-        pool, indptr, indices, last = _sub_pool(case, [i])
-        qn = wl.raw_numpy(case.q[i * Q:(i + 1) * Q], w.q_dtype)
-        pn = wl.raw_numpy(pool, w.kv_dtype)
-        t = time.perf_counter()
-        if Q > 1 or "rope" in kw:
-            oracle.batch_decode_multi(qn, pn, w.layout, indptr, indices, last,
-                                      w.page_size, Q, w.q_dtype, w.kv_dtype,
-                                      w.sm_scale, **kw)
-        elif w.fixed_split_size:
-            oracle.batch_decode_split(qn, pn, w.layout, indptr, indices, last,
-                                      w.page_size, w.q_dtype, w.kv_dtype,
-                                      w.sm_scale, w.fixed_split_size, **kw)
-        else:
-            oracle.batch_decode(qn, pn, w.layout, indptr, indices, last,
-                                w.page_size, w.q_dtype, w.kv_dtype, w.sm_scale,
-                                **kw)
-        elapsed += time.perf_counter() - t
+    pool, indptr, indices, last = _sub_pool(case, [i])
+    qn = wl.raw_numpy(case.q[i * Q:(i + 1) * Q], w.q_dtype)
+    pn = wl.raw_numpy(pool, w.kv_dtype)
+    common = (qn, pn, w.layout, indptr, indices, last, w.page_size)
+    if Q > 1 or w.pos_encoding_mode != "NONE":
+        return lambda: oracle.batch_decode_multi(*common, Q, w.q_dtype, w.kv_dtype,
+                                                 w.sm_scale, **kw)
+    if w.fixed_split_size:
+        return lambda: oracle.batch_decode_split(*common, w.q_dtype, w.kv_dtype,
+                                                 w.sm_scale, w.fixed_split_size, **kw)
+    return lambda: oracle.batch_decode(*common, w.q_dtype, w.kv_dtype, w.sm_scale, **kw)
+
+
+def _timed(calls):
+    """(wall seconds, process CPU seconds) of running every call once."""
+    c0, t0 = time.process_time(), time.perf_counter()
+    for f in calls:
+        f()
+    return time.perf_counter() - t0, time.process_time() - c0
+
+
+def run_cpu_baseline(w, case, budget_s=5.0, one_thread=False):
+    """The fp64 oracle as it stands on a bounded sample of the batch: the
+    requests in batch order until `budget_s` seconds of oracle time have
+    passed (or all), then the same requests twice more; the median of the
+    three runs. ``cores`` is the parallelism the runs actually had (process
+    CPU time / wall time, rounded up), next to the BLAS thread count."""
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threadpool_limits, blas = None, 1
+    Q = w.q_len_per_req
+    calls, tokens, spent = [], 0, 0.0
+    for i in range(w.batch):
+        f = _oracle_call(w, case, i)
+        dt, _ = _timed([f])
+        spent += dt
+        calls.append(f)
         L = int(case.pt.lengths[i])
         s0 = 0 if w.window_left < 0 else max(0, L - Q - w.window_left)
         tokens += L - s0
-        done.append(i)
-        if elapsed >= budget_s:
+        if spent >= budget_s:
             break
-    kvb = tokens * w.num_kv_heads * w.head_dim * 2 * ELEM[w.kv_dtype]
-    other = len(done) * Q * w.num_qo_heads * (w.head_dim * (
-        ELEM[w.q_dtype] + ELEM[w.o_dtype]) + 4)
-    gbs = (kvb + other) / elapsed / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(done)} of {w.batch} requests ({tokens} attended "
-                      f"tokens), fp64 NumPy, {elapsed:.1f} s; host has "
-                      f"{os.cpu_count()} cpus, BLAS threads {threads}"}
+    n = len(calls)
+    nbytes = tokens * w.num_kv_heads * w.head_dim * 2 * ELEM[w.kv_dtype] + \
+        n * Q * w.num_qo_heads * (w.head_dim * (ELEM[w.q_dtype] + ELEM[w.o_dtype]) + 4)
+    runs = [_timed(calls) for _ in range(3)]
+    wall = sorted(r[0] for r in runs)[1]
+    cores = max(1, math.ceil(max(r[1] / r[0] for r in runs) - 0.05))
+    out = {"value": round(nbytes / wall / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+           "kind": "oracle",
+           "sample": f"{n} of {w.batch} requests ({tokens} attended tokens), fp64 "
+                     f"NumPy, median of 3 runs of {wall:.2f} s (spread "
+                     f"{runs_spread(runs)}); host has {os.cpu_count()} cpus, BLAS "
+                     f"threads {blas}"}
+    if one_thread and threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            r1 = sorted(_timed(calls)[0] for _ in range(3))[1]
+        out["value_1thread"] = round(nbytes / r1 / 1e9, 4)
+        out["sample"] += f"; one thread: median of 3 runs of {r1:.2f} s"
+    return out
+
+
+def runs_spread(runs):
+    w = [r[0] for r in runs]
+    return f"{min(w):.2f}-{max(w):.2f} s"
 
 
 def profiled_traffic(workload: str, src_hash: str, launch_bytes: int):
@@ -153,8 +188,14 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="serving_batch",
+    ap.add_argument("--workload", default="gemma2_decode",
                     choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--replays", type=int, default=5,
+                    help="timed replays of the graph holding the K calls")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="calls per step, each on a cache of its own (default: "
+                         "32 for the class example, whose loop runs over 32 "
+                         "layers, else 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (for counter scaling)")
@@ -173,9 +214,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     case = wl.make_case(w, device=dev)
+    layers = args.layers or (32 if w.name == "worked_example" else 1)
     used_bytes = int(case.pt.indptr[-1]) * 2 * w.page_size * w.num_kv_heads * \
         w.head_dim * ELEM[w.kv_dtype]
-    n_pools = max(2, math.ceil(2 * MALL_BYTES / max(used_bytes, 1)))
+    # Distinct K/V pools: one per layer, and at least enough that a step
+    # never finds the previous step's rows in the Infinity Cache.
+    n_pools = max(layers, 2, math.ceil(2 * MALL_BYTES / max(used_bytes * layers, 1)) * layers)
     pools = [case.pool] + [wl.make_pool(w, case.pt.pool_pages, dev,
                                         seed=w.seed + 1000 * k)
                            for k in range(1, n_pools)]
@@ -190,10 +234,13 @@ def main():
         rope_theta=w.rope_theta, rope_scale=w.rope_scale)
     info = plan.info
     rows = w.batch * w.q_len_per_req
-    o = torch.empty((rows, w.num_qo_heads, w.head_dim),
-                    dtype=wl.TORCH_DTYPES[w.o_dtype], device=dev)
-    lse = torch.empty((rows, w.num_qo_heads), dtype=torch.float32,
-                      device=dev)
+    # per layer: its own q and outputs (the class example's loop)
+    qs = [case.q] + [wl.make_q(w, np.random.default_rng(w.seed + 7 * k), device=dev)
+                     for k in range(1, layers)]
+    outs = [(torch.empty((rows, w.num_qo_heads, w.head_dim),
+                         dtype=wl.TORCH_DTYPES[w.o_dtype], device=dev),
+             torch.empty((rows, w.num_qo_heads), dtype=torch.float32, device=dev))
+            for _ in range(layers)]
     ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8,
                      device=dev)
     total_bytes = algorithmic_bytes(w, case.pt)
@@ -205,62 +252,71 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(k, evs=None):
-        pool = pools[k % n_pools]
+    def call(k, evs=None):
+        """Call k: layer k % layers on pool k % n_pools."""
+        li = k % layers
         if evs is not None:
             evs[0].record()
-        plan.run(case.q, pool, k_scale=w.k_scale, v_scale=w.v_scale, out=o,
-                 lse=lse, workspace=ws)
+        plan.run(qs[li], pools[k % n_pools], k_scale=w.k_scale, v_scale=w.v_scale,
+                 out=outs[li][0], lse=outs[li][1], workspace=ws)
         if evs is not None:
             evs[1].record()
 
-    for k in range(args.warmup):
-        step(k)
+    calls = args.steps * layers
+    base = args.warmup * layers
+    for k in range(base):
+        call(k)
     torch.cuda.synchronize()
     # Per-launch kernel time (the roofline): each call launched from the
     # host between two events on the stream it runs on.
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-              for _ in range(args.steps)]
+              for _ in range(calls)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(args.warmup + k, events[k])
+    for k in range(calls):
+        call(base + k, events[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     dec_ms = [e[0].elapsed_time(e[1]) for e in events]
     dec_avg = float(np.mean(dec_ms))
-    eager_us = wall * 1e6 / args.steps
+    eager_us = wall * 1e6 / calls
     launch = "eager"
+    replay_us = [eager_us]
     if not args.eager:
-        # Whole-job throughput: the K calls (the same pool rotation) captured
-        # once in a HIP graph, replayed once untimed and once timed. pkd_run
-        # allocates nothing and never synchronises, so it captures as is.
+        # Whole-job throughput: the K steps' calls (the same pool rotation)
+        # captured once in a HIP graph, replayed once untimed, then R times
+        # under the host clock. pkd_run allocates nothing and never
+        # synchronises, so it captures as is.
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step(0)
+            call(0)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         with torch.cuda.graph(graph):
-            for k in range(args.steps):
-                step(args.warmup + k)
+            for k in range(calls):
+                call(base + k)
         graph.replay()
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        graph.replay()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        replay_us = []
+        for _ in range(max(1, args.replays)):
+            t0 = time.perf_counter()
+            graph.replay()
+            torch.cuda.synchronize()
+            replay_us.append((time.perf_counter() - t0) * 1e6 / calls)
         launch = "hip_graph"
-    ms_step = wall * 1e3 / args.steps
-    value = total_bytes / (ms_step * 1e-3) / 1e9
+    us_call = float(np.median(replay_us))
+    ms_step = us_call * layers / 1e3
+    value = total_bytes / (us_call * 1e-6) / 1e9
     achieved = total_bytes / (dec_avg * 1e-3) / 1e9
     src_hash = kernel_source_hash()
     traffic = profiled_traffic(w.name, src_hash, total_bytes)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = run_cpu_baseline(w, case)
+        cpu = run_cpu_baseline(w, case, one_thread=w.name in ("worked_example",
+                                                              "serving_batch"))
 
     line = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) and "
@@ -271,7 +327,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
-        "us_per_call": round(ms_step * 1e3, 2),
+        "us_per_call": round(us_call, 2),
+        "us_per_call_min_max": [round(min(replay_us), 2), round(max(replay_us), 2)],
+        "replays": len(replay_us) if launch == "hip_graph" else 0,
         "us_per_call_eager": round(eager_us, 2),
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "higher_is_better": True,
@@ -290,6 +348,7 @@ def main():
             "fixed_split_size": w.fixed_split_size,
             "q_len_per_req": w.q_len_per_req,
             "pos_encoding_mode": w.pos_encoding_mode,
+            "layers_per_step": layers,
             "split_pages_used": info.split_pages,
             "work_items": info.num_items,
             "attended_tokens": int(info.attended_tokens),

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define PKD_ABI_VERSION 3
+#define PKD_ABI_VERSION 4
 
 typedef enum {
   PKD_OK = 0,
@@ -59,7 +59,10 @@ typedef enum {
   PKD_EUNSUPPORTED = -2,  /* valid, but not built (head_dim, dtype, ...)  */
   PKD_EHIP = -3,          /* a HIP runtime call failed                    */
   PKD_ENOMEM = -4,        /* host or device allocation failed (plan only) */
-  PKD_EWORKSPACE = -5     /* workspace missing or smaller than required   */
+  PKD_EWORKSPACE = -5,    /* workspace missing or smaller than required   */
+  PKD_EBUSY = -6          /* a run of the plan is still in flight on
+                             another stream (runs of one plan must not
+                             overlap)                                     */
 } pkd_status;
 
 /* Stored element types. E4M3 is the OCP fp8 "fn" format (torch.float8_e4m3fn):
@@ -144,9 +147,13 @@ typedef struct {
 
 typedef struct pkd_plan pkd_plan; /* opaque, owned by the library */
 
+/* Library housekeeping (no passage of the page): PKD_ABI_VERSION of the
+ * built library, for a binding to check against this header. */
 int32_t pkd_abi_version(void);
 
-/* Message of the last failed call on this thread ("" if none). The pointer
+/* Library housekeeping (no passage; the page's wrappers raise exceptions
+ * that name the violated limit, which this message carries to a binding):
+ * message of the last failed call on this thread ("" if none). The pointer
  * stays valid until the next pkd_* call on the same thread. */
 const char* pkd_last_error(void);
 
@@ -230,14 +237,29 @@ pkd_status pkd_plan_create_graph(const pkd_plan_params* params, int32_t max_page
  * plan must be stream-ordered after it (and none may be running). Not
  * capturable. Errors: PKD_EINVAL (not a graph plan, NULL, more than
  * max_pages pages, invalid page table), PKD_EUNSUPPORTED (more units than
- * the capacity; not expected within max_pages), PKD_EHIP. On error the plan
+ * the capacity; not expected within max_pages), PKD_EBUSY (a run of the
+ * plan on another stream is still in flight), PKD_EHIP. On error the plan
  * keeps its previous page table. */
 pkd_status pkd_plan_update(pkd_plan* plan, const int32_t* indptr,
                            const int32_t* last_page_len, void* stream);
 
+/* Size of the workspace pkd_run needs for this plan, in bytes (0 when no
+ * request is split). The decode wrapper's constructor takes the workspace
+ * from the caller (float_workspace_buffer, the buffer that holds split-KV
+ * partial states); this is how a caller sizes it. Errors: PKD_EINVAL for
+ * a NULL argument. */
+pkd_status pkd_plan_workspace_bytes(const pkd_plan* plan, size_t* bytes);
+
+/* What plan() decided (the chunking of fixed_split_size / disable_split_kv
+ * and the planner's own split of the same plan() section), for callers and
+ * tests: unit and workgroup counts, split size, attended tokens, workspace
+ * bytes. Errors: PKD_EINVAL for a NULL argument. */
 pkd_status pkd_plan_get_info(const pkd_plan* plan, pkd_plan_info* info);
 
-/* Waits for the plan's upload to finish, then frees it. NULL is a no-op. */
+/* Library housekeeping (no passage; the counterpart of the wrapper object
+ * going away): waits for the plan's upload to finish, then frees it. The
+ * caller must not destroy a plan whose runs are still in flight. NULL is a
+ * no-op. */
 void pkd_plan_destroy(pkd_plan* plan);
 
 /* run() (flashinfer.decode › BatchDecodeWithPagedKVCacheWrapper › run()):
@@ -269,11 +291,16 @@ void pkd_plan_destroy(pkd_plan* plan);
  * holds in reserve; which workgroup runs a unit never changes the result.
  * Runs of one plan must not overlap in time (for example on two streams):
  * the workgroups share work counters, reserve slots and merge counters
- * owned by the plan. Runs of different plans may overlap.
+ * owned by the plan. Runs of different plans may overlap. A run on a
+ * stream other than that of the plan's previous run fails with PKD_EBUSY
+ * while that previous run has not finished (checked with an event the
+ * library records after each run; runs recorded into a HIP graph are not
+ * tracked, and neither are their replays: a graph's runs of one plan must
+ * be ordered by the caller).
  * Alignment: q, k_cache, v_cache 16 bytes (and page_stride a multiple of 16
  * bytes), o 8 bytes, workspace 256 bytes.
  * Errors: PKD_EINVAL (null pointer, page_stride too small, misaligned
- * buffer), PKD_EWORKSPACE, PKD_EHIP (launch failure). */
+ * buffer), PKD_EWORKSPACE, PKD_EBUSY, PKD_EHIP (launch failure). */
 pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
                    const void* v_cache, int64_t page_stride, float q_scale,
                    float k_scale, float v_scale, const float* sinks, void* o,

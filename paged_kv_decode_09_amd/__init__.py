@@ -18,15 +18,16 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkd.so")
-ABI_VERSION = 3            # PKD_ABI_VERSION of include/pkd.h
+ABI_VERSION = 4            # PKD_ABI_VERSION of include/pkd.h
 
-PKD_OK, PKD_EINVAL, PKD_EUNSUPPORTED, PKD_EHIP, PKD_ENOMEM, PKD_EWORKSPACE = (
-    0, -1, -2, -3, -4, -5)
+PKD_OK, PKD_EINVAL, PKD_EUNSUPPORTED, PKD_EHIP, PKD_ENOMEM, PKD_EWORKSPACE, \
+    PKD_EBUSY = (0, -1, -2, -3, -4, -5, -6)
 PKD_F16, PKD_BF16, PKD_E4M3, PKD_F32 = 0, 1, 2, 3
 PKD_NHD, PKD_HND = 0, 1
 
 _STATUS = {PKD_EINVAL: "EINVAL", PKD_EUNSUPPORTED: "EUNSUPPORTED",
-           PKD_EHIP: "EHIP", PKD_ENOMEM: "ENOMEM", PKD_EWORKSPACE: "EWORKSPACE"}
+           PKD_EHIP: "EHIP", PKD_ENOMEM: "ENOMEM", PKD_EWORKSPACE: "EWORKSPACE",
+           PKD_EBUSY: "EBUSY"}
 
 
 class PkdError(RuntimeError):
@@ -91,6 +92,7 @@ _SIGS = {
                                              ctypes.POINTER(_P)]),
     "pkd_plan_update": (ctypes.c_int, [_P, _P, _P, _P]),
     "pkd_plan_get_info": (ctypes.c_int, [_P, ctypes.POINTER(pkd_plan_info)]),
+    "pkd_plan_workspace_bytes": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),
     "pkd_plan_destroy": (None, [_P]),
     "pkd_run": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_float,
                                ctypes.c_float, ctypes.c_float, _P, _P, _P, _P,
@@ -162,6 +164,21 @@ def _stream_ptr(stream) -> int:
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+def _foreign_stream(stream):
+    """The torch stream `stream` names when it is not torch's current stream,
+    else None. Tensors the binding allocates on the current stream for a run
+    on such a stream are marked as in use on it (record_stream), so that the
+    caching allocator hands their memory to no other tensor before that
+    run's kernel has finished with it."""
+    if stream is None:
+        return None
+    cur = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return None if stream.cuda_stream == cur.cuda_stream else stream
+    ptr = int(stream)
+    return None if ptr == cur.cuda_stream else torch.cuda.ExternalStream(ptr)
 
 
 def make_params(batch_size, num_qo_heads, num_kv_heads, head_dim, page_size,
@@ -338,7 +355,9 @@ class PagedDecodePlan:
 
     @property
     def workspace_bytes(self) -> int:
-        return int(self.info.workspace_bytes)
+        n = ctypes.c_size_t()
+        _check(lib().pkd_plan_workspace_bytes(self._handle, ctypes.byref(n)))
+        return int(n.value)
 
     def update(self, indptr, last_page_len, stream=None) -> None:
         """A graph plan's new page table (pkd_plan_update): same batch size,
@@ -366,14 +385,17 @@ class PagedDecodePlan:
         if _dtype_code(kv_dtype) != p.kv_dtype:
             raise PkdError(PKD_EINVAL, f"cache dtype {kv_dtype} differs from "
                            "the plan")
+        temps = []        # tensors allocated here for this run
         if out is None:
             out = torch.empty((B, nq, hd), dtype=_TORCH_OF[p.o_dtype],
                               device=q.device)
+            temps.append(out)
         elif tuple(out.shape) != (B, nq, hd) or not out.is_contiguous() or \
                 _dtype_code(out.dtype) != p.o_dtype:
             raise PkdError(PKD_EINVAL, "out has the wrong shape or dtype")
         if return_lse and lse is None:
             lse = torch.empty((B, nq), dtype=torch.float32, device=q.device)
+            temps.append(lse)
         elif lse is not None and (tuple(lse.shape) != (B, nq) or
                                   lse.dtype != torch.float32 or
                                   not lse.is_contiguous()):
@@ -381,11 +403,12 @@ class PagedDecodePlan:
         ws_bytes = self.workspace_bytes
         if workspace is None and ws_bytes > 0:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+            temps.append(workspace)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_len = workspace.numel() * workspace.element_size() if \
             workspace is not None else 0
         sc = [1.0 if s is None else float(s) for s in (q_scale, k_scale, v_scale)]
-        return (q, kp, vp, stride, sc, out, lse, ws_ptr, ws_len, workspace)
+        return (q, kp, vp, stride, sc, out, lse, ws_ptr, ws_len, temps)
 
     def run(self, q: torch.Tensor, paged_kv_cache, q_scale=None, k_scale=None,
             v_scale=None, out=None, lse=None, return_lse: bool = False,
@@ -395,8 +418,8 @@ class PagedDecodePlan:
         return_lse. ``sinks``: fp32 device tensor of num_qo_heads values
         ([num_kv_heads, G] or flat), one sink logit per q head."""
         (q, kp, vp, stride, sc, out, lse, ws_ptr, ws_len,
-         _ws) = self._args(q, paged_kv_cache, q_scale, k_scale, v_scale, out,
-                           lse, return_lse or lse is not None, workspace)
+         temps) = self._args(q, paged_kv_cache, q_scale, k_scale, v_scale, out,
+                             lse, return_lse or lse is not None, workspace)
         sink_ptr = None
         if sinks is not None:
             if sinks.dtype != torch.float32 or not sinks.is_cuda or \
@@ -410,7 +433,17 @@ class PagedDecodePlan:
                              sc[0], sc[1], sc[2], sink_ptr, out.data_ptr(),
                              lse.data_ptr() if lse is not None else None,
                              ws_ptr, ws_len, _stream_ptr(stream)))
+        _keep_for_stream(temps, stream)
         return (out, lse) if return_lse else out
+
+
+def _keep_for_stream(temps, stream) -> None:
+    """record_stream on the run's stream for each tensor allocated for the
+    run, when that stream is not torch's current stream."""
+    fs = _foreign_stream(stream) if temps else None
+    if fs is not None:
+        for t in temps:
+            t.record_stream(fs)
 
 
 class BatchDecodeWithPagedKVCacheWrapper:
@@ -584,6 +617,7 @@ def merge_states(v: torch.Tensor, s: torch.Tensor, out_dtype=None,
     _check(lib().pkd_merge_states(v.data_ptr(), s.data_ptr(), rows, n, hd,
                                   v_out.data_ptr(), _dtype_code(od),
                                   s_out.data_ptr(), _stream_ptr(stream)))
+    _keep_for_stream([v_out, s_out], stream)
     return v_out, s_out
 
 

@@ -9,6 +9,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "pkd_internal.h"
 
@@ -18,6 +19,13 @@ struct pkd_plan {
   void* dev = nullptr;                // counters, merge counters, items
   void* staging = nullptr;            // pinned host copy used by the upload
   hipEvent_t uploaded = nullptr;
+  // The last run launched outside graph capture: an event recorded after it
+  // on its stream. A run (or update) on another stream while that event is
+  // pending would share the plan's counters with it, and is refused.
+  mutable std::mutex run_mu;
+  mutable hipEvent_t ran = nullptr;
+  mutable hipStream_t ran_on = nullptr;
+  mutable bool ran_any = false;
   int device = 0;
   int32_t slots = 0;                  // decode workgroups that fit on the GPU
   // A graph plan (pkd_plan_create_graph) keeps its device memory, its launch
@@ -86,6 +94,7 @@ void free_plan(pkd_plan* p) {
     (void)hipEventSynchronize(p->uploaded);
     (void)hipEventDestroy(p->uploaded);
   }
+  if (p->ran != nullptr) (void)hipEventDestroy(p->ran);
   if (p->dev != nullptr) (void)hipFree(p->dev);
   if (p->staging != nullptr) (void)hipHostFree(p->staging);
   delete p;
@@ -139,6 +148,39 @@ pkd_status upload(pkd_plan* p, void* stream) {
     (void)hipStreamSynchronize(hs);
     return hip_fail(e, "uploading the work list");
   }
+  return PKD_OK;
+}
+
+// True when `stream` is being captured into a graph (then no event is
+// queried or recorded: the capture would record or forbid it).
+bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) return true;
+  return cs != hipStreamCaptureStatusNone;
+}
+
+// PKD_EBUSY if the plan's last run went to a stream other than `stream` and
+// has not finished. Caller holds plan->run_mu.
+pkd_status check_not_in_flight(const pkd_plan* plan, hipStream_t stream, const char* what) {
+  if (!plan->ran_any || plan->ran_on == stream) return PKD_OK;
+  const hipError_t q = hipEventQuery(plan->ran);
+  if (q == hipErrorNotReady)
+    return pkd::fail(PKD_EBUSY, std::string(what) + " on a stream other than that of the "
+                                "plan's previous run, which is still in flight: runs of one "
+                                "plan share its work counters and must not overlap");
+  if (q != hipSuccess) return hip_fail(q, "querying the plan's previous run");
+  return PKD_OK;
+}
+
+// Records the end of a run on `stream` (after its launch). Caller holds
+// plan->run_mu.
+pkd_status note_run(const pkd_plan* plan, hipStream_t stream) {
+  hipError_t e = hipSuccess;
+  if (plan->ran == nullptr) e = hipEventCreateWithFlags(&plan->ran, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(plan->ran, stream);
+  if (e != hipSuccess) return hip_fail(e, "recording the run's completion event");
+  plan->ran_on = stream;
+  plan->ran_any = true;
   return PKD_OK;
 }
 
@@ -384,6 +426,12 @@ pkd_status pkd_plan_update(pkd_plan* plan, const int32_t* indptr, const int32_t*
   if (indptr[p.batch_size] > plan->max_pages)
     return pkd::fail(PKD_EINVAL, "the page table holds " + std::to_string(indptr[p.batch_size]) +
                                      " pages > max_pages " + std::to_string(plan->max_pages));
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(plan->run_mu);
+  if (!capturing(hs)) {
+    pkd_status busy = check_not_in_flight(plan, hs, "pkd_plan_update");
+    if (busy != PKD_OK) return busy;
+  }
   pkd::HostPlan h;
   pkd_status st = pkd::build_host_plan(p, indptr, last_page_len, plan->slots, &h);
   if (st != PKD_OK) return st;
@@ -406,6 +454,13 @@ pkd_status pkd_plan_get_info(const pkd_plan* plan, pkd_plan_info* info) {
   if (plan == nullptr || info == nullptr)
     return pkd::fail(PKD_EINVAL, "plan and info must not be NULL");
   *info = plan->host.info;
+  return PKD_OK;
+}
+
+pkd_status pkd_plan_workspace_bytes(const pkd_plan* plan, size_t* bytes) {
+  if (plan == nullptr || bytes == nullptr)
+    return pkd::fail(PKD_EINVAL, "plan and bytes must not be NULL");
+  *bytes = plan->host.info.workspace_bytes;
   return PKD_OK;
 }
 
@@ -475,9 +530,19 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
   if (sinks != nullptr && reinterpret_cast<uintptr_t>(sinks) % 4 != 0)
     return pkd::fail(PKD_EINVAL, "sinks must be 4-byte aligned");
   a.sinks = sinks;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (capturing(hs)) {
+    // recorded into a graph: its replays are not tracked
+    int e = pkd::launch_decode(p, a, plan->host.info.num_workgroups, stream);
+    if (e != hipSuccess) return hip_fail((hipError_t)e, "decode launch");
+    return PKD_OK;
+  }
+  std::lock_guard<std::mutex> lock(plan->run_mu);
+  pkd_status busy = check_not_in_flight(plan, hs, "pkd_run");
+  if (busy != PKD_OK) return busy;
   int e = pkd::launch_decode(p, a, plan->host.info.num_workgroups, stream);
   if (e != hipSuccess) return hip_fail((hipError_t)e, "decode launch");
-  return PKD_OK;
+  return note_run(plan, hs);
 }
 
 pkd_status pkd_merge_states(const float* v, const float* s, int32_t rows,

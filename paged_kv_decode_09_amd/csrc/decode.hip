@@ -1173,12 +1173,16 @@ DecodeFn pick_kernel(const pkd_plan_params& p) {
 
 }  // namespace
 
+// Launches return the status of their own launch call (hipLaunchKernel),
+// so an earlier, unrelated error pending on the thread is neither reported
+// as theirs nor cleared.
 int launch_decode(const pkd_plan_params& p, const DecodeArgs& a, int32_t num_workgroups,
                   void* stream) {
   if (num_workgroups <= 0) return hipSuccess;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(pick_kernel(p), dim3(num_workgroups), dim3(kWaves * 64), 0, s, a);
-  return hipGetLastError();
+  DecodeArgs arg = a;
+  void* params[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(pick_kernel(p)), dim3(num_workgroups),
+                         dim3(kWaves * 64), params, 0, reinterpret_cast<hipStream_t>(stream));
 }
 
 int32_t decode_wgs_per_cu(const pkd_plan_params& p) {
@@ -1193,8 +1197,10 @@ int launch_merge(const MergeArgs& a, void* stream) {
   if (a.num_rows <= 0) return hipSuccess;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   dim3 grid((a.num_rows + kMergeRowsPerBlock - 1) / kMergeRowsPerBlock);
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(kMergeRowsPerBlock * 64), 0, s, a);
-  return hipGetLastError();
+  MergeArgs arg = a;
+  void* params[] = {&arg};
+  return hipLaunchKernel(reinterpret_cast<const void*>(merge_kernel), grid,
+                         dim3(kMergeRowsPerBlock * 64), params, 0, s);
 }
 
 }  // namespace pkd

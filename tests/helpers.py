@@ -95,3 +95,86 @@ def oracle_for(w, case, requests=None, split_pages=None, q=None):
 def max_abs(gpu: torch.Tensor, ref: np.ndarray) -> float:
     g = gpu.detach().float().cpu().double().numpy()
     return float(np.max(np.abs(g - ref))) if ref.size else 0.0
+
+
+def oracle_all(w, case, chunk=32, q=None):
+    """oracle_for over every request of the batch, `chunk` requests at a
+    time (bounds the host copy of the pages)."""
+    outs, lses = [], []
+    for r0 in range(0, w.batch, chunk):
+        o, l = oracle_for(w, case, range(r0, min(w.batch, r0 + chunk)), q=q)
+        outs.append(o)
+        lses.append(l)
+    return np.concatenate(outs), np.concatenate(lses)
+
+
+def _rne_error_var(x, dtype):
+    """Variance of the error of rounding x (fp64) to nearest-even in `dtype`,
+    with the error taken as uniform over one unit in the last place:
+    ulp(x)^2 / 12, ulp(x) = 2^(floor(log2|x|) - (p - 1)) with p = 8
+    significant bits (bf16) or 11 (f16), and the format's smallest
+    spacing below its normal range."""
+    p, emin = (8, -126) if dtype == "bf16" else (11, -14)
+    ax = np.abs(x)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    e = np.maximum(e, emin)
+    ulp = np.exp2(e - (p - 1))
+    return np.where(ax > 0, ulp * ulp / 12.0, 0.0)
+
+
+def rope_lse_bounds(w, case, requests, theta, scale, base=LSE_TOL, sigmas=6.0):
+    """Per-row lse bound for ROPE_LLAMA runs, [len(requests) * Q, nq].
+
+    With ROPE_LLAMA the kernel rounds the rotated q (once per unit) and each
+    rotated key element to the MFMA operand type (the q dtype) before the
+    dot product; the unrotated path never rounds its operands. Rounding
+    error delta of an element x is modelled as independent, zero-mean,
+    variance ulp(x)^2/12 (round to nearest even). A logit's error is then
+    dx_t = sm * sum_d (dq_d k'_td + q'_d dk_td), and to first order the lse
+    moves by sum_t p_t dx_t (p the softmax weights), whose variance is
+        sm^2 [ sum_d var(dq_d) (sum_t p_t k'_td)^2
+               + sum_t p_t^2 sum_d q'_d^2 var(dk_td) ]
+    (the q error is shared by every token, the key errors are not). The
+    bound is the plain path's lse tolerance plus `sigmas` standard
+    deviations of that error; q', k' and p are the exact fp64 values (the
+    soft cap's derivative, at most 1, is left out, which only widens the
+    bound)."""
+    import oracle as orc
+    Q = w.q_len_per_req
+    reqs = list(requests)
+    pool, indptr, indices, last = sub_pool(case, reqs)
+    rows = torch.tensor(rows_of(w, reqs))
+    qn = orc.widen(wl.raw_numpy(case.q[rows], w.q_dtype), w.q_dtype)
+    pn = wl.raw_numpy(pool, w.kv_dtype)
+    kc = pn[:, 0]
+    lens = orc.kv_lengths(indptr, last, w.page_size)
+    nq, nkv, hd = w.num_qo_heads, w.num_kv_heads, w.head_dim
+    G = nq // nkv
+    sm = w.sm_scale
+    out = np.zeros((len(reqs) * Q, nq))
+    for r in range(len(reqs)):
+        i = r
+        L = int(lens[i])
+        K, _ = orc.gather_request(kc, kc, w.layout, indices, indptr, i, L, w.page_size)
+        Kf = orc.widen(K, w.kv_dtype, w.k_scale)                 # [L, nkv, hd]
+        for j in range(Q):
+            pos = L - Q + j
+            s0 = 0 if w.window_left < 0 else max(0, pos - w.window_left)
+            Kr = orc.rope_rotate(Kf[s0:pos + 1].transpose(1, 0, 2),
+                                 np.arange(s0, pos + 1), theta, scale)  # [nkv, n, hd]
+            vk = _rne_error_var(Kr / w.k_scale, w.q_dtype) * w.k_scale ** 2
+            qr = orc.rope_rotate(qn[r * Q + j][:, None, :], [pos], theta, scale)[:, 0, :]
+            vq = _rne_error_var(qr, w.q_dtype)
+            for hq in range(nq):
+                h = hq // G
+                x = sm * (Kr[h] @ qr[hq])
+                if w.logits_soft_cap > 0:
+                    x = w.logits_soft_cap * np.tanh(x / w.logits_soft_cap)
+                p = np.exp(x - x.max())
+                p /= p.sum()
+                kbar = p @ Kr[h]                                  # [hd]
+                var = sm * sm * (np.sum(vq[hq] * kbar * kbar) +
+                                 np.sum(p * p * (vk[h] @ (qr[hq] * qr[hq]))))
+                out[r * Q + j, hq] = base + sigmas * np.sqrt(var)
+    return out

@@ -23,10 +23,10 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     lib = pkd.lib()
     names = header_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for name in names:
         assert hasattr(lib, name), name
-    assert lib.pkd_abi_version() == pkd.ABI_VERSION == 3
+    assert lib.pkd_abi_version() == pkd.ABI_VERSION == 4
 
 
 def test_struct_sizes_match_header():
@@ -318,3 +318,40 @@ def test_block_table_errors(lens, max_blocks, needle):
         pkd.plan_query_block_table(lens, max_blocks, 256, num_qo_heads=8,
                                    num_kv_heads=2, head_dim=128, page_size=16)
     assert needle in str(e.value) and e.value.status == pkd.PKD_EINVAL
+
+
+def test_workspace_bytes_rejects_null_arguments():
+    lib = pkd.lib()
+    n = ctypes.c_size_t(7)
+    assert lib.pkd_plan_workspace_bytes(None, ctypes.byref(n)) == pkd.PKD_EINVAL
+    assert b"must not be NULL" in lib.pkd_last_error()
+    assert n.value == 7
+
+
+class _FakeStream:
+    def __init__(self, ptr):
+        self.cuda_stream = ptr
+
+
+class _FakeTensor:
+    def __init__(self):
+        self.recorded = []
+
+    def record_stream(self, s):
+        self.recorded.append(s)
+
+
+def test_temporaries_are_kept_for_a_run_on_another_stream(monkeypatch):
+    """Tensors the binding allocates for a run (out, lse, workspace) are
+    marked in use on the run's stream when that is not torch's current
+    stream, and left alone when it is (or when none is given)."""
+    import torch
+    cur = _FakeStream(11)
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda: cur)
+    monkeypatch.setattr(torch.cuda, "ExternalStream", lambda ptr: ("external", ptr))
+    for stream, expect in ((None, []), (11, []), (22, [("external", 22)])):
+        ts = [_FakeTensor(), _FakeTensor()]
+        pkd._keep_for_stream(ts, stream)
+        assert all(t.recorded == expect for t in ts), (stream, ts[0].recorded)
+    # nothing allocated: nothing to record, and the stream is not looked up
+    pkd._keep_for_stream([], 22)

@@ -1,10 +1,11 @@
 """GPU tests at the full sizes of the named workloads, in the launch
 configuration bench.py times, plus bit-exact gather probes and determinism.
 
-Full-size parity compares sampled requests (the oracle computes them one by
-one) and checks a property on every request: with q = 0 every logit is 0, so
-lse = ln(#attended tokens), which pins each request's length, page count and
-window edge to the token."""
+Full-size parity compares o and lse with the oracle on every request of the
+batch, and checks a property that pins each request's length: with q = 0
+every logit is 0, so lse = ln(#attended tokens), which fixes its length,
+page count and window edge to the token (a dropped or doubled token moves o
+by only about 1/L, below the o tolerance on long requests)."""
 import math
 
 import numpy as np
@@ -12,7 +13,7 @@ import pytest
 import torch
 
 from paged_kv_decode_09_amd import workloads as wl
-from helpers import LSE_TOL, max_abs, o_tol, oracle_for, plan_for, run_gpu
+from helpers import LSE_TOL, max_abs, o_tol, oracle_all, oracle_for, plan_for, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -37,13 +38,9 @@ def test_full_size_workload(name):
     o, lse, plan = run_gpu(w, case)
     assert not torch.isnan(o).any() and not torch.isnan(lse).any()
     L = case.pt.lengths
-    rng = np.random.default_rng(99)
-    reqs = sorted({0, w.batch - 1, int(np.argmin(L)), int(np.argmax(L)),
-                   *rng.choice(w.batch, 2, replace=False).tolist()})
-    ref_o, ref_l = oracle_for(w, case, reqs)
-    idx = torch.tensor(reqs)
-    eo, el = max_abs(o[idx], ref_o), max_abs(lse[idx], ref_l)
-    say(name, "requests", reqs, "o max-abs", eo, "lse max-abs", el,
+    ref_o, ref_l = oracle_all(w, case)
+    eo, el = max_abs(o, ref_o), max_abs(lse, ref_l)
+    say(name, "all", w.batch, "requests: o max-abs", eo, "lse max-abs", el,
         "split", plan.info.split_pages, "items", plan.info.num_items)
     assert eo <= o_tol(w) and el <= LSE_TOL
     # q = 0: lse = ln(n) on every request, to within half the gap to n +- 1

@@ -697,3 +697,87 @@ def test_rope_decode_matches_sdpa_on_rotated_inputs():
     qr = rot(q[0], L - 1)
     ref = sdpa_decode(qr, Kr, V, 0.25)
     assert np.max(np.abs(o[0] - ref)) < 1e-12
+
+
+def _rot_complex(x, positions, theta, scale):
+    """Independent rotation: pairs (x[i], x[i + hd/2]) as complex numbers
+    times e^{i * position / scale * theta^(-2i/hd)}; x [n, ..., hd]."""
+    hd = x.shape[-1]
+    half = hd // 2
+    ang = np.asarray(positions, np.float64)[:, None] / scale * \
+        theta ** (-2.0 * np.arange(half) / hd)[None, :]
+    w = np.exp(1j * ang).reshape((len(positions),) + (1,) * (x.ndim - 2) + (half,))
+    z = (x[..., :half] + 1j * x[..., half:]) * w
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def _rope_sdpa_reference(q_rows, K, V, L, Q, sm, theta, scale, window):
+    """SDPA (fp64) over every key of the request rotated at its absolute
+    token index 0..L-1, query token j rotated at L-Q+j, with the prefill
+    page's causal mask (diagonal kv_len - qo_len) and the inclusive window;
+    lse from torch.logsumexp over the same masked logits."""
+    Kr = _rot_complex(K, np.arange(L), theta, scale)             # [L, nkv, hd]
+    qr = _rot_complex(q_rows, np.arange(L - Q, L), theta, scale)  # [Q, nq, hd]
+    mask = prefill_causal_mask(Q, L, window)
+    o = sdpa_masked(qr, Kr, V, sm, mask)
+    nq, nkv = q_rows.shape[1], K.shape[1]
+    Ke = torch.from_numpy(np.repeat(Kr, nq // nkv, axis=1).transpose(1, 0, 2).copy())
+    logits = sm * torch.einsum("jhd,htd->jht", torch.from_numpy(qr), Ke)
+    logits = logits.masked_fill(~torch.from_numpy(mask)[:, None, :], -math.inf)
+    return o, torch.logsumexp(logits, dim=-1).numpy()
+
+
+def _rope_window_case(Q, window, seed):
+    rng = np.random.default_rng(seed)
+    nkv, group, hd = 2, 2, 16
+    lengths = [Q + window + 9, 57, Q]     # windows that start past 0, and a full one
+    K = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    V = [rng.standard_normal((L, nkv, hd)) for L in lengths]
+    q = rng.standard_normal((len(lengths) * Q, nkv * group, hd))
+    cache, indptr, indices, last = scatter_to_pages(K, V, "NHD", 4, 40, rng)
+    return lengths, K, V, q, (cache, indptr, indices, last)
+
+
+@pytest.mark.parametrize("Q,window", [(1, 5), (1, 20), (3, 4), (4, 0), (2, 11)])
+def test_rope_with_window_and_several_tokens_matches_sdpa_at_absolute_positions(Q, window):
+    """ROPE_LLAMA under a window and with q_len_per_req > 1: keys keep their
+    absolute token index as position (not an index relative to the window
+    start) and query token j sits at L-Q+j."""
+    theta, scale, sm = 300.0, 1.5, 0.3
+    lengths, K, V, q, (cache, indptr, indices, last) = _rope_window_case(Q, window, 70 + Q)
+    o, lse = oracle.batch_decode_multi(q, cache, "NHD", indptr, indices, last, 4, Q,
+                                       "f64", "f64", sm, window_left=window,
+                                       rope=(theta, scale))
+    for i, L in enumerate(lengths):
+        ro, rl = _rope_sdpa_reference(q[i * Q:(i + 1) * Q], K[i], V[i], L, Q, sm,
+                                      theta, scale, window)
+        assert np.max(np.abs(o[i * Q:(i + 1) * Q] - ro)) < 1e-12
+        assert np.max(np.abs(lse[i * Q:(i + 1) * Q] - rl)) < 1e-12
+    if Q == 1:
+        # the one-token entry point gives the same
+        o1, l1 = oracle.batch_decode(q, cache, "NHD", indptr, indices, last, 4, "f64",
+                                     "f64", sm, window_left=window, rope=(theta, scale))
+        assert np.max(np.abs(o1 - o)) < 1e-12 and np.max(np.abs(l1 - lse)) < 1e-12
+
+
+def test_rope_window_pin_rejects_window_relative_key_positions(monkeypatch):
+    """The pin above fails for an oracle that rotates keys at positions
+    counted from the window start (a planted mistake in the oracle)."""
+    import oracle.oracle as om
+    real = om.rope_rotate
+
+    def relative(x, positions, rope_theta=1e4, rope_scale=1.0):
+        p = np.asarray(positions)
+        if p.size > 1:                        # the keys: shift to the window start
+            p = p - p[0]
+        return real(x, p, rope_theta, rope_scale)
+
+    monkeypatch.setattr(om, "rope_rotate", relative)
+    theta, scale, sm, Q, window = 300.0, 1.5, 0.3, 1, 5
+    lengths, K, V, q, (cache, indptr, indices, last) = _rope_window_case(Q, window, 71)
+    o, _ = oracle.batch_decode_multi(q, cache, "NHD", indptr, indices, last, 4, Q,
+                                     "f64", "f64", sm, window_left=window,
+                                     rope=(theta, scale))
+    ro, _ = _rope_sdpa_reference(q[:Q], K[0], V[0], lengths[0], Q, sm, theta, scale,
+                                 window)
+    assert np.max(np.abs(o[:Q] - ro)) > 1e-2

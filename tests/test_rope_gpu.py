@@ -8,7 +8,8 @@ import torch
 
 import oracle
 from paged_kv_decode_09_amd import workloads as wl
-from helpers import LSE_TOL, max_abs, o_tol, oracle_for, plan_for, run_gpu, sub_pool
+from helpers import (max_abs, o_tol, oracle_all, plan_for, rope_lse_bounds, run_gpu,
+                     sub_pool)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,20 +35,21 @@ def check_rope(w, case, theta, scale, split, reqs=None):
         v_scale=w.v_scale, rope=(theta, scale))
     idx = torch.tensor(rows)
     assert not torch.isnan(o).any()
-    eo, el = max_abs(o[idx], ref_o), max_abs(lse[idx], ref_l)
-    say("o max-abs", eo, "lse max-abs", el)
+    eo = max_abs(o[idx], ref_o)
+    check_rope_lse(w, case, reqs, lse[idx], ref_l, theta, scale)
+    say("o max-abs", eo)
     assert eo <= o_tol(w), eo
-    assert el <= rope_lse_tol(w), el
 
 
-def rope_lse_tol(w):
-    """The rotated q and keys are rounded to the MFMA operand type (the q
-    dtype), which the unrotated path never does: each logit then carries an
-    error of about sm_scale * sqrt(2 head_dim / 3) * u on N(0, 1) data
-    (u = 2^-9 for bf16, 2^-12 for f16), ~1.6e-3 at head_dim 128 in bf16, and
-    so does the lse. With bf16 operands the lse bound is the bf16 o bound,
-    1e-2; with f16 operands it stays LSE_TOL (the error is 8x smaller)."""
-    return 1e-2 if w.q_dtype == "bf16" else LSE_TOL
+def check_rope_lse(w, case, reqs, lse_gpu, ref_l, theta, scale):
+    """Every row's lse error within its own derived bound (helpers.
+    rope_lse_bounds: the plain tolerance plus six standard deviations of
+    the error that rounding the rotated operands to the q dtype adds)."""
+    err = np.abs(lse_gpu.double().cpu().numpy() - ref_l)
+    bound = rope_lse_bounds(w, case, reqs, theta, scale)
+    say("lse max-abs", float(err.max()), "worst err/bound", float(np.max(err / bound)),
+        "bounds", float(bound.min()), "..", float(bound.max()))
+    assert np.all(err <= bound), float(np.max(err / bound))
 
 
 @pytest.mark.parametrize("hd,kv,Q,cap,window,layout", [
@@ -83,17 +85,14 @@ def test_rope_at_long_positions(kv):
 
 def test_serving_rope_full_size():
     """The serving batch with RoPE at full size, in the launch configuration
-    of the bench, on sampled requests (the oracle computes them one by one)."""
+    of the bench, against the oracle on every request."""
     w = wl.WORKLOADS["serving_rope"]
     say(w.name)
     case = wl.make_case(w, device="cuda")
     o, lse, plan = run_gpu(w, case)
     assert not torch.isnan(o).any() and not torch.isnan(lse).any()
-    L = case.pt.lengths
-    reqs = sorted({0, w.batch - 1, int(np.argmin(L)), int(np.argmax(L)), 21})
-    ref_o, ref_l = oracle_for(w, case, reqs)
-    idx = torch.tensor(reqs)
-    eo, el = max_abs(o[idx], ref_o), max_abs(lse[idx], ref_l)
-    say(w.name, "requests", reqs, "o max-abs", eo, "lse max-abs", el,
-        "items", plan.info.num_items)
-    assert eo <= o_tol(w) and el <= rope_lse_tol(w)
+    ref_o, ref_l = oracle_all(w, case)
+    eo = max_abs(o, ref_o)
+    say(w.name, "all", w.batch, "requests: o max-abs", eo, "items", plan.info.num_items)
+    assert eo <= o_tol(w)
+    check_rope_lse(w, case, range(w.batch), lse, ref_l, w.rope_theta, w.rope_scale)
