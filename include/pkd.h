@@ -307,6 +307,27 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
                    float* lse, void* workspace, size_t workspace_bytes,
                    void* stream);
 
+/* pkd_run without a workspace argument, for callers that cannot allocate
+ * one: code being captured into a HIP graph, tight serving loops, harnesses
+ * that forbid device allocation. The split-KV partial states go to a static
+ * workspace the library holds on each GPU it runs on (PKD_STATIC_WORKSPACE_BYTES,
+ * 32 MiB, kept until the process ends); this call allocates nothing and
+ * computes exactly what pkd_run computes with the same plan (the same
+ * kernel and bits). The workspace needs no clearing: every partial state is
+ * written before it is read, and the counters are the plan's.
+ * All calls on one GPU share that GPU's static workspace, so calls that
+ * overlap in time on one GPU (two streams, or two host threads) race, even
+ * for different plans; order them. The current device must be the plan's.
+ * Arguments as pkd_run. Errors: as pkd_run, and PKD_EWORKSPACE when the
+ * plan needs more than PKD_STATIC_WORKSPACE_BYTES (pkd_plan_workspace_bytes
+ * tells beforehand), PKD_EINVAL when the current device is not the plan's,
+ * PKD_EHIP when the static workspace's address is unavailable. */
+#define PKD_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+pkd_status pkd_run_static_workspace(const pkd_plan* plan, const void* q, const void* k_cache,
+                                    const void* v_cache, int64_t page_stride, float q_scale,
+                                    float k_scale, float v_scale, const float* sinks,
+                                    void* o, float* lse, void* stream);
+
 /* merge_states (named with fixed_split_size in plan()): combine `num_states`
  * attention states per row by log-sum-exp:
  *   M = max_k s[k];  Z = sum_k exp(s[k] - M);  s_out = M + ln Z;

@@ -97,6 +97,9 @@ _SIGS = {
     "pkd_run": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64, ctypes.c_float,
                                ctypes.c_float, ctypes.c_float, _P, _P, _P, _P,
                                ctypes.c_size_t, _P]),
+    "pkd_run_static_workspace": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int64,
+                                                ctypes.c_float, ctypes.c_float,
+                                                ctypes.c_float, _P, _P, _P, _P]),
     "pkd_merge_states": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, _P, ctypes.c_int32, _P,
                                         _P]),
@@ -371,7 +374,7 @@ class PagedDecodePlan:
         _check(lib().pkd_plan_get_info(self._handle, ctypes.byref(self.info)))
 
     def _args(self, q, paged_kv_cache, q_scale, k_scale, v_scale, out, lse,
-              return_lse, workspace):
+              return_lse, workspace, allocate_workspace=True):
         p = self.params
         # q, o and lse hold q_len_per_req rows per request
         B = p.batch_size * max(1, p.q_len_per_req)
@@ -401,7 +404,7 @@ class PagedDecodePlan:
                                   not lse.is_contiguous()):
             raise PkdError(PKD_EINVAL, f"lse must be contiguous fp32 [{B}, {nq}]")
         ws_bytes = self.workspace_bytes
-        if workspace is None and ws_bytes > 0:
+        if workspace is None and ws_bytes > 0 and allocate_workspace:
             workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
             temps.append(workspace)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -420,21 +423,44 @@ class PagedDecodePlan:
         (q, kp, vp, stride, sc, out, lse, ws_ptr, ws_len,
          temps) = self._args(q, paged_kv_cache, q_scale, k_scale, v_scale, out,
                              lse, return_lse or lse is not None, workspace)
-        sink_ptr = None
-        if sinks is not None:
-            if sinks.dtype != torch.float32 or not sinks.is_cuda or \
-                    not sinks.is_contiguous() or \
-                    sinks.numel() != self.params.num_qo_heads:
-                raise PkdError(PKD_EINVAL, "sinks must be a contiguous fp32 "
-                               f"device tensor of {self.params.num_qo_heads} "
-                               "values")
-            sink_ptr = sinks.data_ptr()
+        sink_ptr = self._sink_ptr(sinks)
         _check(lib().pkd_run(self._handle, q.data_ptr(), kp, vp, stride,
                              sc[0], sc[1], sc[2], sink_ptr, out.data_ptr(),
                              lse.data_ptr() if lse is not None else None,
                              ws_ptr, ws_len, _stream_ptr(stream)))
         _keep_for_stream(temps, stream)
         return (out, lse) if return_lse else out
+
+    def run_static_workspace(self, q: torch.Tensor, paged_kv_cache, q_scale=None,
+                             k_scale=None, v_scale=None, out=None, lse=None,
+                             return_lse: bool = False, stream=None,
+                             sinks: Optional[torch.Tensor] = None):
+        """run() through pkd_run_static_workspace: the split-KV partial states
+        go to the library's static workspace on the GPU instead of a caller's
+        workspace, so the call allocates nothing when ``out`` (and ``lse``,
+        if wanted) are given. Calls that overlap on one GPU share that
+        workspace and race."""
+        (q, kp, vp, stride, sc, out, lse, _ws_ptr, _ws_len,
+         temps) = self._args(q, paged_kv_cache, q_scale, k_scale, v_scale, out,
+                             lse, return_lse or lse is not None, None,
+                             allocate_workspace=False)
+        _check(lib().pkd_run_static_workspace(
+            self._handle, q.data_ptr(), kp, vp, stride, sc[0], sc[1], sc[2],
+            self._sink_ptr(sinks), out.data_ptr(),
+            lse.data_ptr() if lse is not None else None, _stream_ptr(stream)))
+        _keep_for_stream(temps, stream)
+        return (out, lse) if return_lse else out
+
+    def _sink_ptr(self, sinks):
+        if sinks is None:
+            return None
+        if sinks.dtype != torch.float32 or not sinks.is_cuda or \
+                not sinks.is_contiguous() or \
+                sinks.numel() != self.params.num_qo_heads:
+            raise PkdError(PKD_EINVAL, "sinks must be a contiguous fp32 "
+                           f"device tensor of {self.params.num_qo_heads} "
+                           "values")
+        return sinks.data_ptr()
 
 
 def _keep_for_stream(temps, stream) -> None:

@@ -297,6 +297,10 @@ pkd_status create_plan(const pkd_plan_params* params, const int32_t* indptr,
   }
   p->indices = indices;
   p->device = dev;
+  // The static workspace's device address on this device (looked up once
+  // per device, here, outside any graph capture). A failed lookup only
+  // disables pkd_run_static_workspace, which then reports it.
+  (void)pkd::static_scratch_resolve(dev);
   if (graph_max_pages > 0) {
     int64_t total = 0, one = 0;
     graph_capacities(*params, graph_max_pages, &total, &one);
@@ -466,11 +470,15 @@ pkd_status pkd_plan_workspace_bytes(const pkd_plan* plan, size_t* bytes) {
 
 void pkd_plan_destroy(pkd_plan* plan) { free_plan(plan); }
 
-pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
-                   const void* v_cache, int64_t page_stride, float q_scale,
-                   float k_scale, float v_scale, const float* sinks, void* o,
-                   float* lse, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+pkd_status run_impl(const pkd_plan* plan, const void* q, const void* k_cache,
+                    const void* v_cache, int64_t page_stride, float q_scale,
+                    float k_scale, float v_scale, const float* sinks, void* o,
+                    float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   pkd_status st = check_run(plan, q, k_cache, v_cache, page_stride, o, workspace,
                             workspace_bytes);
   if (st != PKD_OK) return st;
@@ -543,6 +551,46 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
   int e = pkd::launch_decode(p, a, plan->host.info.num_workgroups, stream);
   if (e != hipSuccess) return hip_fail((hipError_t)e, "decode launch");
   return note_run(plan, hs);
+}
+
+}  // namespace
+
+extern "C" {
+
+pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
+                   const void* v_cache, int64_t page_stride, float q_scale,
+                   float k_scale, float v_scale, const float* sinks, void* o,
+                   float* lse, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return run_impl(plan, q, k_cache, v_cache, page_stride, q_scale, k_scale, v_scale, sinks,
+                  o, lse, workspace, workspace_bytes, stream);
+}
+
+pkd_status pkd_run_static_workspace(const pkd_plan* plan, const void* q, const void* k_cache,
+                                    const void* v_cache, int64_t page_stride, float q_scale,
+                                    float k_scale, float v_scale, const float* sinks,
+                                    void* o, float* lse, void* stream) {
+  if (plan == nullptr) return pkd::fail(PKD_EINVAL, "plan is NULL (run before plan)");
+  const size_t need = plan->host.info.workspace_bytes;
+  if (need > pkd::kStaticScratchBytes)
+    return pkd::fail(PKD_EWORKSPACE,
+                     "the plan needs a workspace of " + std::to_string(need) +
+                         " bytes, more than the static workspace's " +
+                         std::to_string(pkd::kStaticScratchBytes) +
+                         "; use pkd_run with a workspace of that size");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != plan->device)
+    return pkd::fail(PKD_EINVAL, "the current device (" + std::to_string(dev) +
+                                     ") is not the plan's (" + std::to_string(plan->device) +
+                                     ")");
+  void* ws = pkd::static_scratch_address(dev);
+  if (ws == nullptr)
+    return pkd::fail(PKD_EHIP, "the static workspace's device address could not be "
+                               "looked up on device " + std::to_string(dev));
+  return run_impl(plan, q, k_cache, v_cache, page_stride, q_scale, k_scale, v_scale, sinks,
+                  o, lse, ws, pkd::kStaticScratchBytes, stream);
 }
 
 pkd_status pkd_merge_states(const float* v, const float* s, int32_t rows,

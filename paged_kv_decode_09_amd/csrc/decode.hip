@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "pkd_internal.h"
 
@@ -1191,6 +1192,37 @@ int32_t decode_wgs_per_cu(const pkd_plan_params& p) {
           &blocks, reinterpret_cast<const void*>(pick_kernel(p)), kWaves * 64, 0) != hipSuccess)
     return 0;
   return blocks;
+}
+
+// ---------------------------------------------------------------------------
+// Static workspace of pkd_run_static_workspace: split-KV partial states of
+// one run at a time per GPU. Each GPU the library runs on holds its own
+// copy, at its own device address, until the process ends. In host code
+// `scratch` names a host-side stand-in, never the device memory: only the
+// address hipGetSymbolAddress returns is passed to kernels.
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+int static_scratch_resolve(int device) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[device] != nullptr) return hipSuccess;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch[device] = ptr;
+  return hipSuccess;
+}
+
+void* static_scratch_address(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch[device];
 }
 
 int launch_merge(const MergeArgs& a, void* stream) {

@@ -183,4 +183,15 @@ int launch_decode(const pkd_plan_params& p, const DecodeArgs& a,
 int32_t decode_wgs_per_cu(const pkd_plan_params& p);
 int launch_merge(const MergeArgs& a, void* stream);
 
+// The library's static workspace (decode.hip): a file-scope device array of
+// kStaticScratchBytes that pkd_run_static_workspace uses in place of a
+// caller's workspace. static_scratch_resolve looks up its device address on
+// the current device (once per device; the array's host-side name is not a
+// device address); static_scratch_address returns what was resolved for
+// `device` (NULL if never resolved or the lookup failed). Returns a
+// hipError_t value as int.
+constexpr size_t kStaticScratchBytes = PKD_STATIC_WORKSPACE_BYTES;
+int static_scratch_resolve(int device);
+void* static_scratch_address(int device);
+
 }  // namespace pkd

@@ -23,7 +23,7 @@ def header_functions():
 def test_library_exports_every_declared_symbol():
     lib = pkd.lib()
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for name in names:
         assert hasattr(lib, name), name
     assert lib.pkd_abi_version() == pkd.ABI_VERSION == 4

@@ -1,0 +1,75 @@
+"""pkd_run_static_workspace (GPU): the run entry point that takes no
+workspace and allocates nothing, for callers that cannot allocate. It must
+give exactly what pkd_run gives with the same plan, on two calls in a row
+(the second with a smaller batch, while the static workspace still holds the
+first call's partial states), and refuse a plan whose workspace exceeds the
+static one. Every test prints its case before it touches the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_decode_09_amd as pkd
+from paged_kv_decode_09_amd import workloads as wl
+from helpers import LSE_TOL, max_abs, o_tol, oracle_all, plan_for
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def both_ways(w, case):
+    plan = plan_for(w, case)
+    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    ref, rl = plan.run(case.q, case.pool, k_scale=w.k_scale, v_scale=w.v_scale,
+                       return_lse=True, workspace=ws)
+    o, lse = torch.empty_like(ref), torch.empty_like(rl)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    plan.run_static_workspace(case.q, case.pool, k_scale=w.k_scale, v_scale=w.v_scale,
+                              out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+    return plan, ref, rl, o, lse
+
+
+@pytest.mark.parametrize("split", [16, 0])
+def test_static_workspace_run_equals_run_on_two_calls(split):
+    big = wl.small_workload(seed=83, batch=6, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                            q_dtype="bf16", kv_dtype="bf16", o_dtype="bf16", layout="HND",
+                            lengths=("fixed", [5000, 70, 12000, 4096, 1, 3000]),
+                            fixed_split_size=split)
+    small = wl.small_workload(seed=84, batch=3, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                              q_dtype="bf16", kv_dtype="bf16", o_dtype="bf16", layout="HND",
+                              lengths=("fixed", [2000, 33, 700]), fixed_split_size=split)
+    for w in (big, small):
+        say(w)
+        case = wl.make_case(w, device="cuda")
+        plan, ref, rl, o, lse = both_ways(w, case)
+        say("partials", plan.info.num_partials, "workspace bytes", plan.workspace_bytes)
+        assert torch.equal(o, ref) and torch.equal(lse, rl)
+        eo_ref, el_ref = oracle_all(w, case)
+        assert max_abs(o, eo_ref) <= o_tol(w) and max_abs(lse, el_ref) <= LSE_TOL
+
+
+def test_static_workspace_run_full_size_serving_batch():
+    w = wl.WORKLOADS["serving_batch"]
+    say(w.name)
+    case = wl.make_case(w, device="cuda")
+    plan, ref, rl, o, lse = both_ways(w, case)
+    say("partials", plan.info.num_partials, "workspace bytes", plan.workspace_bytes)
+    assert plan.info.num_partials > 0
+    assert torch.equal(o, ref) and torch.equal(lse, rl)
+
+
+def test_static_workspace_refuses_a_plan_that_needs_more():
+    w = wl.small_workload(seed=85, batch=2, num_qo_heads=64, num_kv_heads=8, head_dim=128,
+                          lengths=("fixed", [60000, 3001]), fixed_split_size=1)
+    say(w)
+    case = wl.make_case(w, device="cuda")
+    plan = plan_for(w, case)
+    assert plan.workspace_bytes > (32 << 20)
+    with pytest.raises(pkd.PkdError) as e:
+        plan.run_static_workspace(case.q, case.pool)
+    assert e.value.status == pkd.PKD_EWORKSPACE and "static workspace" in str(e.value)
