@@ -131,15 +131,46 @@ __device__ __forceinline__ typename Op<BF16>::v8 e4m3x8(unsigned lo, unsigned hi
   return __builtin_bit_cast(typename Op<BF16>::v8, r);
 }
 
+// The values of x in a lane and in the lane 16 (or 32) away, from gfx950's
+// row exchanges on two copies of x. v_permlane16_swap swaps the odd 16-lane rows
+// of its first operand with the even rows of its second, v_permlane32_swap
+// the upper half of the first with the lower half of the second; on two
+// copies of x, lane l of the two results then holds {x[l], x[l ^ 16]} (or
+// {x[l], x[l ^ 32]}), in some order. No lane index, no LDS round trip. The
+// copies are made opaque first: the compiler would otherwise take the
+// exchange of two equal operands for a no-op.
+template <bool kHalves>
+__device__ __forceinline__ f32x2 lane_pair(float x) {
+  unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+  asm volatile("" : "+v"(a));
+  asm volatile("" : "+v"(b));
+  // (the elements are copied out before any bit cast: a bit cast applied to
+  // an element of the returned vector reads element 0)
+  unsigned lo, hi;
+  if constexpr (kHalves) {
+    auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    lo = r[0];
+    hi = r[1];
+  } else {
+    auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    lo = r[0];
+    hi = r[1];
+  }
+  return (f32x2){__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi)};
+}
+// Reductions over the four 16-lane groups; max and + are commutative, so
+// every lane gets the same bits as from x op x[l ^ 16], then op x[l ^ 32].
 __device__ __forceinline__ float wave_max_over_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  f32x2 p = lane_pair<false>(x);
+  x = fmaxf(p[0], p[1]);
+  p = lane_pair<true>(x);
+  return fmaxf(p[0], p[1]);
 }
 __device__ __forceinline__ float wave_sum_over_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  f32x2 p = lane_pair<false>(x);
+  x = p[0] + p[1];
+  p = lane_pair<true>(x);
+  return p[0] + p[1];
 }
 
 // Device-scope (agent) relaxed atomic store: it bypasses the caches that are
