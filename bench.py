@@ -18,8 +18,9 @@ Prints one JSON line. ``value`` is the achieved HBM bandwidth of the whole
 call: algorithmic bytes / wall time per call, with the K timed calls replayed
 from one HIP graph (the way a serving loop issues its decode steps; pkd_run
 allocates nothing and never synchronises, so it captures unchanged); the
-graph is replayed R times and the median replay is reported, with the
-fastest and slowest beside it. ``--eager`` times K host launches instead.
+graph is replayed R times, after 0.2 s of untimed replays that bring the
+GPU's clocks to their steady state, and the median replay is reported, with
+the fastest and slowest beside it. ``--eager`` times K host launches instead.
 Algorithmic bytes = K and V rows of the attended tokens (each read once per
 kv head) + q + o + fp32 lse + the page indices of the touched pages + indptr
 + last_page_len. ``roofline`` is that kernel, timed with HIP events on the
@@ -46,6 +47,7 @@ import paged_kv_decode_09_amd as pkd  # noqa: E402
 from paged_kv_decode_09_amd import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+WARM_S = 0.2
 MALL_BYTES = 256 << 20
 ELEM = {"f16": 2, "bf16": 2, "e4m3": 1}
 
@@ -295,6 +297,17 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
         launch = "hip_graph"
+    # Steady state: the GPU's clocks drop while it idles (the capture above)
+    # and take tens of milliseconds of back-to-back work to ramp up again, so
+    # the timed regions follow at least WARM_S seconds of untimed ones.
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < WARM_S:
+        if graph is not None:
+            graph.replay()
+        else:
+            for k in range(calls):
+                call(base + k)
+        torch.cuda.synchronize()
     # Each timed region (one graph replay, or K eager launches) runs on
     # torch's current stream, where the kernels run, bracketed by two HIP
     # events (the kernel time, K launches back to back, and the gaps between
