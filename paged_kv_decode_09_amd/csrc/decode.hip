@@ -406,7 +406,7 @@ struct Win {
 };
 
 template <int HD, bool QBF16, bool KV8, bool CAP, bool ROPE>
-__global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void decode_kernel(DecodeArgs args) {
+__global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) void decode_kernel(DecodeArgs args) {
   DecodeArgs a = args;
   if (args.plan_header != nullptr) {
     // a graph plan: the launch was recorded once; the current page table's
@@ -604,11 +604,20 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
         *reinterpret_cast<u32x4*>(kl + off) = st.k[i / kNP][i % kNP];
         *reinterpret_cast<u32x4*>(vl + off) = st.v[i / kNP][i % kNP];
       }
+    // (With the rotary embedding at head_dim 256 and 16-bit K the pieces are
+    // read pair by pair inside the rotation below: all sixteen at once would
+    // not leave the registers the rotation needs.)
+    constexpr bool kPieceByPiece = ROPE && HD == 256 && !KV8;
     u32x4 kr[2][kNP];
+    auto read_piece = [&](int tile, int p) {
+      return *reinterpret_cast<const u32x4*>(kl + (tile ? tau1 : tau0) * G_::kVPitch + 64 * p + 16 * g);
+    };
+    if constexpr (!kPieceByPiece) {
 #pragma unroll
-    for (int p = 0; p < kNP; ++p) {
-      kr[0][p] = *reinterpret_cast<const u32x4*>(kl + tau0 * G_::kVPitch + 64 * p + 16 * g);
-      kr[1][p] = *reinterpret_cast<const u32x4*>(kl + tau1 * G_::kVPitch + 64 * p + 16 * g);
+      for (int p = 0; p < kNP; ++p) {
+        kr[0][p] = read_piece(0, p);
+        kr[1][p] = read_piece(1, p);
+      }
     }
     if constexpr (ROPE) {
       // q at its query position, once per unit (its loads have landed by
@@ -632,6 +641,13 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
       sc[1] = sc[0];
 #pragma unroll
       for (int j = 0; j < kHalf; ++j) {
+        if constexpr (kPieceByPiece) {
+          // 16-bit K at head_dim 256: piece j and j + kHalf of both tiles
+          kr[0][j] = read_piece(0, j);
+          kr[0][j + kHalf] = read_piece(0, j + kHalf);
+          kr[1][j] = read_piece(1, j);
+          kr[1][j + kHalf] = read_piece(1, j + kHalf);
+        }
         v8 lo0 = k_operand(kr, 0, j), hi0 = k_operand(kr, 0, j + kHalf);
         v8 lo1 = k_operand(kr, 1, j), hi1 = k_operand(kr, 1, j + kHalf);
 #pragma unroll
@@ -864,9 +880,12 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
         // at or below num_qo_heads; the heads past it take odd powers of
         // 2^(-4/n2))
         const int hq = cu.kv_head * group + col_head;
-        const int n2 = 1 << (31 - __builtin_clz(a.num_qo_heads));
-        const float ex = hq < n2 ? -8.0f * (float)(hq + 1) / (float)n2
-                                 : -4.0f * (float)(2 * (hq - n2) + 1) / (float)n2;
+        const int lg2 = 31 - __builtin_clz(a.num_qo_heads);
+        const int n2 = 1 << lg2;
+        // (dividing by the power of two n2 is the exact product with 2^-lg2)
+        const float inv_n2 = __builtin_ldexpf(1.0f, -lg2);
+        const float ex = hq < n2 ? -8.0f * (float)(hq + 1) * inv_n2
+                                 : -4.0f * (float)(2 * (hq - n2) + 1) * inv_n2;
         col_slope = fast_exp2(ex) * (CAP ? 1.0f : kLog2e);
       }
 #pragma unroll
@@ -990,8 +1009,14 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8)) void d
 #pragma unroll
           for (int i = 0; i < 4; ++i) sacc[n * HD + 16 * b + 4 * g + i] = acc[b][i];
         if (g == 0) {
-          s_m[wave][n] = m_run;
-          s_d[wave][n] = d_run;
+          // (the row index, n, is taken from the hardware lane id here, so
+          // that neither it nor these two addresses are kept in registers
+          // through the step loop)
+          unsigned id;
+          asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(id));
+          const int row = (int)(id & 15);
+          s_m[wave][row] = m_run;
+          s_d[wave][row] = d_run;
         }
       }
       lds_barrier();

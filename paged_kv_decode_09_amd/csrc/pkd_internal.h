@@ -50,9 +50,10 @@ constexpr int64_t kStealMinBytes = 512 << 10;
 // compute unit already keeps several times the loads in flight that HBM
 // needs to stream at full rate; more only lengthens the queues, and with
 // them every dependent load at a unit boundary. Head_dim 64 (a quarter of
-// the bytes per step) uses three.
-constexpr int decode_waves_per_simd(int head_dim, bool kv8) {
-  return (void)kv8, head_dim >= 128 ? 1 : 3;
+// the bytes per step) uses three, or two with 16-bit K/V and the rotary
+// embedding, whose rotation needs more registers than a third of the file.
+constexpr int decode_waves_per_simd(int head_dim, bool kv8, bool rope) {
+  return head_dim >= 128 ? 1 : (rope && !kv8 ? 2 : 3);
 }
 
 // One split request: its workspace slots are partial_base ..
