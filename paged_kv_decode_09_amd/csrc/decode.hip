@@ -708,13 +708,19 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
       psum += x[e];
     }
     d_run = d_run * alpha + psum;
-    u32x4 pw;
-    pw[0] = O::pack(x[0], x[1]);
-    pw[1] = O::pack(x[2], x[3]);
-    pw[2] = O::pack(x[4], x[5]);
-    pw[3] = O::pack(x[6], x[7]);
+    // P^T in the operand type as an unevaluated sum hi + lo: hi = p rounded,
+    // lo = the rest rounded. P.V then errs by about 2^-16 of |p| (bf16) rather
+    // than the 2^-9 of hi alone, which, with one or two dominant tokens, would
+    // be as large as the output's own rounding.
+    u32x4 pw, pwl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pw[i] = O::pack(x[2 * i], x[2 * i + 1]);
     const v8 pop = __builtin_bit_cast(v8, pw);
-    // ---- O^T += V^T P^T, one MFMA per 16 hd columns
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pwl[i] = O::pack(x[2 * i] - (float)pop[2 * i], x[2 * i + 1] - (float)pop[2 * i + 1]);
+    const v8 pop_lo = __builtin_bit_cast(v8, pwl);
+    // ---- O^T += V^T P^T, two MFMAs (hi, lo) per 16 hd columns
 #pragma unroll
     for (int b = 0; b < G_::kPvMfma; ++b) {
       v8 vop;
@@ -732,6 +738,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
       }
       f32x4 c = acc[b];
       c[0] *= alpha; c[1] *= alpha; c[2] *= alpha; c[3] *= alpha;
+      c = O::mfma(vop, pop_lo, c);
       acc[b] = O::mfma(vop, pop, c);
     }
   };

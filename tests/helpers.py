@@ -178,3 +178,19 @@ def rope_lse_bounds(w, case, requests, theta, scale, base=LSE_TOL, sigmas=6.0):
                                  np.sum(p * p * (vk[h] @ (qr[hq] * qr[hq]))))
                 out[r * Q + j, hq] = base + sigmas * np.sqrt(var)
     return out
+
+
+def o_bounds(w, ref):
+    """Elementwise bound on |o - ref| for an output of dtype w.o_dtype: the
+    max-abs tolerance, or, where the exact value is too large in magnitude
+    for that tolerance to be reachable, half a unit in the last place of the
+    exact value in the output dtype (the error of rounding it to nearest)
+    plus 1e-4 for the fp32 arithmetic before the rounding. For bf16 that
+    widens the 1e-2 bound only where |o| >= 4 (a half ulp of 2^-6 there);
+    for f16 the 2e-3 bound where |o| >= 8."""
+    p = 8 if w.o_dtype == "bf16" else 11
+    ax = np.abs(np.asarray(ref, dtype=np.float64))
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    half_ulp = np.where(ax > 0, np.exp2(e - (p - 1)) / 2, 0.0)
+    return np.maximum(o_tol(w), half_ulp + 1e-4)

@@ -47,3 +47,18 @@ def test_rope_lse_model_matches_simulated_operand_rounding(dt, hd, window):
             assert abs(rounded - exact) <= bound[i, hq]
             z.append((rounded - exact) / sigma[i, hq])
     assert 0.5 < float(np.std(z)) < 1.5, np.std(z)
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_o_bounds_cover_output_rounding(dt):
+    """helpers.o_bounds admits the rounding of exact outputs to the output
+    dtype (what a perfect kernel would write), and equals the plain max-abs
+    tolerance wherever that rounding stays below it."""
+    from helpers import O_TOL, o_bounds
+    w = wl.small_workload(q_dtype=dt, kv_dtype=dt, o_dtype=dt)
+    x = np.random.default_rng(5).standard_normal(200000) * 4.0
+    r = torch.from_numpy(x).to(torch.bfloat16 if dt == "bf16" else torch.float16).double().numpy()
+    b = o_bounds(w, x)
+    assert np.all(np.abs(r - x) <= b)
+    small = np.abs(x) < (4.0 if dt == "bf16" else 4.0)
+    assert np.all(b[small] == O_TOL[dt])
