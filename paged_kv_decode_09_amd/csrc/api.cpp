@@ -172,16 +172,12 @@ pkd_status check_not_in_flight(const pkd_plan* plan, hipStream_t stream, const c
   return PKD_OK;
 }
 
-// Records the end of a run on `stream` (after its launch). Caller holds
-// plan->run_mu.
-pkd_status note_run(const pkd_plan* plan, hipStream_t stream) {
-  hipError_t e = hipSuccess;
-  if (plan->ran == nullptr) e = hipEventCreateWithFlags(&plan->ran, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventRecord(plan->ran, stream);
-  if (e != hipSuccess) return hip_fail(e, "recording the run's completion event");
+// Records the end of a run on `stream`, after its launch. Caller holds
+// plan->run_mu. Should the record fail, the run (already launched) goes
+// untracked: the next run is not checked against it.
+void note_run(const pkd_plan* plan, hipStream_t stream) {
+  plan->ran_any = plan->ran != nullptr && hipEventRecord(plan->ran, stream) == hipSuccess;
   plan->ran_on = stream;
-  plan->ran_any = true;
-  return PKD_OK;
 }
 
 pkd_status check_run(const pkd_plan* plan, const void* q, const void* k,
@@ -325,6 +321,11 @@ pkd_status create_plan(const pkd_plan_params* params, const int32_t* indptr,
     p->host.info.workspace_bytes =
         pkd::workspace_lse_offset(p->cap_partials, Q * params->num_qo_heads, params->head_dim) +
         (size_t)p->cap_partials * Q * params->num_qo_heads * 4;
+  }
+  e = hipEventCreateWithFlags(&p->ran, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    free_plan(p);
+    return hip_fail(e, "creating the plan's run event");
   }
   const size_t bytes = plan_bytes(*p);
   if (bytes > 0) {
@@ -550,7 +551,8 @@ pkd_status run_impl(const pkd_plan* plan, const void* q, const void* k_cache,
   if (busy != PKD_OK) return busy;
   int e = pkd::launch_decode(p, a, plan->host.info.num_workgroups, stream);
   if (e != hipSuccess) return hip_fail((hipError_t)e, "decode launch");
-  return note_run(plan, hs);
+  note_run(plan, hs);
+  return PKD_OK;
 }
 
 }  // namespace
