@@ -12,21 +12,28 @@
 // fixed_split_size); merge_kernel is the same step as a standalone call.
 //
 // Design (MI355X-first, not the page's):
-//  * One workgroup of 4 wavefronts per work item. Wavefront w takes the
-//    32-token steps w, w+4, ... of the item; the four partial states are
-//    merged in LDS in wavefront order at the end, so the result depends only
-//    on the item's token range (bitwise batch invariance under a fixed split).
-//  * q.K^T on MFMA 16x16x32: K rows are the A operand and arrive straight
-//    from HBM in 16-byte loads (one row segment per lane); the G <= 16 query
-//    rows of the kv head are the B operand (columns past G are zero).
-//    Result lane l holds the logits of tokens 8*(l/16)+4*tile+i for head l%16.
-//  * P.V on MFMA as O^T = V^T P^T. P^T is exactly what each lane holds after
-//    the softmax, so it needs no data movement; V^T comes from a per-wave LDS
-//    copy of the step's V rows read with ds_read_b64_tr_b16 (16-bit V) or
-//    ds_read_b64_tr_b8 (E4M3 V, converted after the read).
+//  * A persistent grid of workgroups of 4 wavefronts, one per compute unit
+//    (three at head_dim 64), that pipeline work items taken from a counter.
+//    Wavefront w takes the 32-token steps w, w+4, ... of an item; the four
+//    partial states are merged in LDS in wavefront order at the end, so the
+//    result depends only on the item's token range (bitwise batch invariance
+//    under a fixed split).
+//  * K and V rows arrive as whole 128-byte lines (non-temporal 16-byte loads,
+//    8 rows per load instruction) into registers, one step ahead, and go to
+//    the wave's LDS copies of the step.
+//  * q.K^T on MFMA 16x16x32: K rows, read back from LDS in the operand
+//    layout, are the A operand; the G*Q <= 16 query rows of the kv head are
+//    the B operand (columns past them repeat row 0 and are never written).
+//    Result lane l holds the logits of tokens 8*(l/16)+4*tile+i for row l%16.
+//  * P.V on MFMA as O^T = V^T P^T. P^T is what each lane holds after the
+//    softmax, so it needs no data movement; it enters as a hi + lo pair in
+//    the operand type (two MFMAs). V^T comes from the LDS copy of the step's
+//    V rows read with ds_read_b64_tr_b16 (16-bit V) or ds_read_b64_tr_b8
+//    (E4M3 V, converted after the read).
 //  * Online softmax in base 2 (v_exp_f32): one running max per head, made
-//    uniform across the four lane groups with two cross-lane maxima per step;
-//    the running sum stays per lane and is reduced once at the end.
+//    uniform across the four lane groups with two cross-lane maxima per step
+//    (gfx950 row exchanges); the running sum stays per lane and is reduced
+//    once at the end.
 //  * Tokens outside [token_begin, token_end) are masked by a select, and their
 //    loads are clamped onto the chunk's own tokens, so stale or NaN slots of a
 //    page are never read.
@@ -711,14 +718,20 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
     // P^T in the operand type as an unevaluated sum hi + lo: hi = p rounded,
     // lo = the rest rounded. P.V then errs by about 2^-16 of |p| (bf16) rather
     // than the 2^-9 of hi alone, which, with one or two dominant tokens, would
-    // be as large as the output's own rounding.
+    // be as large as the output's own rounding. With RoPE the rotated q and
+    // keys are rounded to the operand type already, which moves each p by as
+    // much; hi alone serves there (the second MFMA and its operand would cost
+    // that VALU-bound instance 2 % and buy no accuracy).
+    constexpr bool kPLo = !ROPE;
     u32x4 pw, pwl;
 #pragma unroll
     for (int i = 0; i < 4; ++i) pw[i] = O::pack(x[2 * i], x[2 * i + 1]);
     const v8 pop = __builtin_bit_cast(v8, pw);
+    if constexpr (kPLo) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      pwl[i] = O::pack(x[2 * i] - (float)pop[2 * i], x[2 * i + 1] - (float)pop[2 * i + 1]);
+      for (int i = 0; i < 4; ++i)
+        pwl[i] = O::pack(x[2 * i] - (float)pop[2 * i], x[2 * i + 1] - (float)pop[2 * i + 1]);
+    }
     const v8 pop_lo = __builtin_bit_cast(v8, pwl);
     // ---- O^T += V^T P^T, two MFMAs (hi, lo) per 16 hd columns
 #pragma unroll
@@ -738,7 +751,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
       }
       f32x4 c = acc[b];
       c[0] *= alpha; c[1] *= alpha; c[2] *= alpha; c[3] *= alpha;
-      c = O::mfma(vop, pop_lo, c);
+      if constexpr (kPLo) c = O::mfma(vop, pop_lo, c);
       acc[b] = O::mfma(vop, pop, c);
     }
   };
