@@ -59,10 +59,7 @@ typedef enum {
   PKD_EUNSUPPORTED = -2,  /* valid, but not built (head_dim, dtype, ...)  */
   PKD_EHIP = -3,          /* a HIP runtime call failed                    */
   PKD_ENOMEM = -4,        /* host or device allocation failed (plan only) */
-  PKD_EWORKSPACE = -5,    /* workspace missing or smaller than required   */
-  PKD_EBUSY = -6          /* a run of the plan is still in flight on
-                             another stream (runs of one plan must not
-                             overlap)                                     */
+  PKD_EWORKSPACE = -5     /* workspace missing or smaller than required   */
 } pkd_status;
 
 /* Stored element types. E4M3 is the OCP fp8 "fn" format (torch.float8_e4m3fn):
@@ -233,13 +230,13 @@ pkd_status pkd_plan_create_graph(const pkd_plan_params* params, int32_t max_page
 
 /* A new page table for a graph plan (same parameters and batch size):
  * plans it on the host, waits for the plan's previous upload, and uploads
- * the new work list on `stream` into the same device memory. Runs of the
- * plan must be stream-ordered after it (and none may be running). Not
- * capturable. Errors: PKD_EINVAL (not a graph plan, NULL, more than
- * max_pages pages, invalid page table), PKD_EUNSUPPORTED (more units than
- * the capacity; not expected within max_pages), PKD_EBUSY (a run of the
- * plan on another stream is still in flight), PKD_EHIP. On error the plan
- * keeps its previous page table. */
+ * the new work list on `stream` into the same device memory, ordered (on
+ * the GPU) after the plan's last tracked run. Runs of the plan must be
+ * stream-ordered after it, and replays of graphs holding its runs must not
+ * be in flight. Not capturable. Errors: PKD_EINVAL (not a graph plan, NULL,
+ * more than max_pages pages, invalid page table), PKD_EUNSUPPORTED (more
+ * units than the capacity; not expected within max_pages), PKD_EHIP. On
+ * error the plan keeps its previous page table. */
 pkd_status pkd_plan_update(pkd_plan* plan, const int32_t* indptr,
                            const int32_t* last_page_len, void* stream);
 
@@ -289,18 +286,17 @@ void pkd_plan_destroy(pkd_plan* plan);
  * result does not depend on which workgroup ran which unit.
  * Workgroups that run out of units may take a long unit another workgroup
  * holds in reserve; which workgroup runs a unit never changes the result.
- * Runs of one plan must not overlap in time (for example on two streams):
- * the workgroups share work counters, reserve slots and merge counters
- * owned by the plan. Runs of different plans may overlap. A run on a
- * stream other than that of the plan's previous run fails with PKD_EBUSY
- * while that previous run has not finished (checked with an event the
- * library records after each run; runs recorded into a HIP graph are not
- * tracked, and neither are their replays: a graph's runs of one plan must
- * be ordered by the caller).
+ * Runs of one plan never overlap in time: the workgroups share work
+ * counters, reserve slots and merge counters owned by the plan, so a run
+ * on a stream other than that of the plan's previous run first waits, on
+ * the GPU, for that run (an event the library records after each run; no
+ * host synchronisation). Runs of different plans may overlap. Runs
+ * recorded into a HIP graph, and their replays, are not tracked: a graph's
+ * runs of one plan must be ordered by the caller.
  * Alignment: q, k_cache, v_cache 16 bytes (and page_stride a multiple of 16
  * bytes), o 8 bytes, workspace 256 bytes.
  * Errors: PKD_EINVAL (null pointer, page_stride too small, misaligned
- * buffer), PKD_EWORKSPACE, PKD_EBUSY, PKD_EHIP (launch failure). */
+ * buffer), PKD_EWORKSPACE, PKD_EHIP (launch failure). */
 pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
                    const void* v_cache, int64_t page_stride, float q_scale,
                    float k_scale, float v_scale, const float* sinks, void* o,
@@ -315,9 +311,12 @@ pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
  * computes exactly what pkd_run computes with the same plan (the same
  * kernel and bits). The workspace needs no clearing: every partial state is
  * written before it is read, and the counters are the plan's.
- * All calls on one GPU share that GPU's static workspace, so calls that
- * overlap in time on one GPU (two streams, or two host threads) race, even
- * for different plans; order them. The current device must be the plan's.
+ * All calls on one GPU share that GPU's static workspace, for any plan, so
+ * a call on a stream other than that of the previous such call on the GPU
+ * first waits, on the GPU, for it (as runs of one plan do). Calls recorded
+ * into a HIP graph, and their replays, are not tracked: they race with any
+ * other use of the static workspace that overlaps them. The current device
+ * must be the plan's.
  * Arguments as pkd_run. Errors: as pkd_run, and PKD_EWORKSPACE when the
  * plan needs more than PKD_STATIC_WORKSPACE_BYTES (pkd_plan_workspace_bytes
  * tells beforehand), PKD_EINVAL when the current device is not the plan's,

@@ -20,14 +20,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkd.so")
 ABI_VERSION = 4            # PKD_ABI_VERSION of include/pkd.h
 
-PKD_OK, PKD_EINVAL, PKD_EUNSUPPORTED, PKD_EHIP, PKD_ENOMEM, PKD_EWORKSPACE, \
-    PKD_EBUSY = (0, -1, -2, -3, -4, -5, -6)
+PKD_OK, PKD_EINVAL, PKD_EUNSUPPORTED, PKD_EHIP, PKD_ENOMEM, PKD_EWORKSPACE = (
+    0, -1, -2, -3, -4, -5)
 PKD_F16, PKD_BF16, PKD_E4M3, PKD_F32 = 0, 1, 2, 3
 PKD_NHD, PKD_HND = 0, 1
 
 _STATUS = {PKD_EINVAL: "EINVAL", PKD_EUNSUPPORTED: "EUNSUPPORTED",
-           PKD_EHIP: "EHIP", PKD_ENOMEM: "ENOMEM", PKD_EWORKSPACE: "EWORKSPACE",
-           PKD_EBUSY: "EBUSY"}
+           PKD_EHIP: "EHIP", PKD_ENOMEM: "ENOMEM", PKD_EWORKSPACE: "EWORKSPACE"}
 
 
 class PkdError(RuntimeError):
@@ -438,8 +437,8 @@ class PagedDecodePlan:
         """run() through pkd_run_static_workspace: the split-KV partial states
         go to the library's static workspace on the GPU instead of a caller's
         workspace, so the call allocates nothing when ``out`` (and ``lse``,
-        if wanted) are given. Calls that overlap on one GPU share that
-        workspace and race."""
+        if wanted) are given. Such calls on different streams are ordered
+        on the GPU by the library; calls recorded into graphs are not."""
         (q, kp, vp, stride, sc, out, lse, _ws_ptr, _ws_len,
          temps) = self._args(q, paged_kv_cache, q_scale, k_scale, v_scale, out,
                              lse, return_lse or lse is not None, None,

@@ -13,19 +13,31 @@
 
 #include "pkd_internal.h"
 
+namespace {
+
+// Stream order of the launches that share some device state (a plan's
+// counters, or a GPU's static workspace): an event recorded after the last
+// such launch on its stream. A launch on another stream first waits for that
+// event on the GPU, so launches that share the state never overlap, with no
+// host synchronisation. Launches recorded into a HIP graph are not tracked.
+struct RunOrder {
+  std::mutex mu;
+  hipEvent_t ev = nullptr;    // created before the first launch
+  hipStream_t on = nullptr;   // stream of the last tracked launch
+  bool any = false;           // ev holds the last tracked launch
+};
+
+}  // namespace
+
 struct pkd_plan {
   pkd::HostPlan host;
   const int32_t* indices = nullptr;   // borrowed device pointer
   void* dev = nullptr;                // counters, merge counters, items
   void* staging = nullptr;            // pinned host copy used by the upload
   hipEvent_t uploaded = nullptr;
-  // The last run launched outside graph capture: an event recorded after it
-  // on its stream. A run (or update) on another stream while that event is
-  // pending would share the plan's counters with it, and is refused.
-  mutable std::mutex run_mu;
-  mutable hipEvent_t ran = nullptr;
-  mutable hipStream_t ran_on = nullptr;
-  mutable bool ran_any = false;
+  // Runs share the plan's work, reserve and merge counters: a run (or an
+  // update) on another stream than the previous run is ordered after it.
+  mutable RunOrder order;
   int device = 0;
   int32_t slots = 0;                  // decode workgroups that fit on the GPU
   // A graph plan (pkd_plan_create_graph) keeps its device memory, its launch
@@ -94,7 +106,7 @@ void free_plan(pkd_plan* p) {
     (void)hipEventSynchronize(p->uploaded);
     (void)hipEventDestroy(p->uploaded);
   }
-  if (p->ran != nullptr) (void)hipEventDestroy(p->ran);
+  if (p->order.ev != nullptr) (void)hipEventDestroy(p->order.ev);
   if (p->dev != nullptr) (void)hipFree(p->dev);
   if (p->staging != nullptr) (void)hipHostFree(p->staging);
   delete p;
@@ -159,25 +171,36 @@ bool capturing(hipStream_t stream) {
   return cs != hipStreamCaptureStatusNone;
 }
 
-// PKD_EBUSY if the plan's last run went to a stream other than `stream` and
-// has not finished. Caller holds plan->run_mu.
-pkd_status check_not_in_flight(const pkd_plan* plan, hipStream_t stream, const char* what) {
-  if (!plan->ran_any || plan->ran_on == stream) return PKD_OK;
-  const hipError_t q = hipEventQuery(plan->ran);
-  if (q == hipErrorNotReady)
-    return pkd::fail(PKD_EBUSY, std::string(what) + " on a stream other than that of the "
-                                "plan's previous run, which is still in flight: runs of one "
-                                "plan share its work counters and must not overlap");
-  if (q != hipSuccess) return hip_fail(q, "querying the plan's previous run");
+// Makes `stream` wait on the GPU for the last launch tracked by `r` when
+// that went to another stream. Caller holds r.mu.
+pkd_status order_after(RunOrder& r, hipStream_t stream, const char* what) {
+  if (!r.any || r.on == stream) return PKD_OK;
+  const hipError_t e = hipStreamWaitEvent(stream, r.ev, 0);
+  if (e != hipSuccess) return hip_fail(e, what);
   return PKD_OK;
 }
 
-// Records the end of a run on `stream`, after its launch. Caller holds
-// plan->run_mu. Should the record fail, the run (already launched) goes
-// untracked: the next run is not checked against it.
-void note_run(const pkd_plan* plan, hipStream_t stream) {
-  plan->ran_any = plan->ran != nullptr && hipEventRecord(plan->ran, stream) == hipSuccess;
-  plan->ran_on = stream;
+// Records a launch just made on `stream`. Caller holds r.mu. Should the
+// record fail, the launch (already made) goes untracked: the next launch on
+// another stream is then not ordered after it.
+void note_launch(RunOrder& r, hipStream_t stream) {
+  r.any = r.ev != nullptr && hipEventRecord(r.ev, stream) == hipSuccess;
+  r.on = stream;
+}
+
+// The order of the launches that use a GPU's static workspace
+// (pkd_run_static_workspace, for plans of any kind); its event is created
+// with the first plan made on the device.
+constexpr int kMaxDevices = 64;
+RunOrder g_static_order[kMaxDevices];
+
+pkd_status prepare_static_order(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return PKD_OK;
+  std::lock_guard<std::mutex> lock(g_static_order[dev].mu);
+  if (g_static_order[dev].ev != nullptr) return PKD_OK;
+  const hipError_t e = hipEventCreateWithFlags(&g_static_order[dev].ev, hipEventDisableTiming);
+  if (e != hipSuccess) return hip_fail(e, "creating the static workspace's order event");
+  return PKD_OK;
 }
 
 pkd_status check_run(const pkd_plan* plan, const void* q, const void* k,
@@ -322,10 +345,16 @@ pkd_status create_plan(const pkd_plan_params* params, const int32_t* indptr,
         pkd::workspace_lse_offset(p->cap_partials, Q * params->num_qo_heads, params->head_dim) +
         (size_t)p->cap_partials * Q * params->num_qo_heads * 4;
   }
-  e = hipEventCreateWithFlags(&p->ran, hipEventDisableTiming);
-  if (e != hipSuccess) {
+  e = hipEventCreateWithFlags(&p->order.ev, hipEventDisableTiming);
+  if (e == hipSuccess) {
+    const pkd_status so = prepare_static_order(dev);
+    if (so != PKD_OK) {
+      free_plan(p);
+      return so;
+    }
+  } else {
     free_plan(p);
-    return hip_fail(e, "creating the plan's run event");
+    return hip_fail(e, "creating the plan's order event");
   }
   const size_t bytes = plan_bytes(*p);
   if (bytes > 0) {
@@ -432,10 +461,11 @@ pkd_status pkd_plan_update(pkd_plan* plan, const int32_t* indptr, const int32_t*
     return pkd::fail(PKD_EINVAL, "the page table holds " + std::to_string(indptr[p.batch_size]) +
                                      " pages > max_pages " + std::to_string(plan->max_pages));
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  std::lock_guard<std::mutex> lock(plan->run_mu);
+  std::lock_guard<std::mutex> lock(plan->order.mu);
   if (!capturing(hs)) {
-    pkd_status busy = check_not_in_flight(plan, hs, "pkd_plan_update");
-    if (busy != PKD_OK) return busy;
+    // the upload overwrites what an earlier run on another stream may still read
+    pkd_status ord = order_after(plan->order, hs, "ordering the update after the plan's last run");
+    if (ord != PKD_OK) return ord;
   }
   pkd::HostPlan h;
   pkd_status st = pkd::build_host_plan(p, indptr, last_page_len, plan->slots, &h);
@@ -475,11 +505,13 @@ void pkd_plan_destroy(pkd_plan* plan) { free_plan(plan); }
 
 namespace {
 
+// `shared`: the order of a device state beyond the plan's that the run uses
+// (the static workspace), or NULL.
 pkd_status run_impl(const pkd_plan* plan, const void* q, const void* k_cache,
                     const void* v_cache, int64_t page_stride, float q_scale,
                     float k_scale, float v_scale, const float* sinks, void* o,
                     float* lse, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+                    void* stream, RunOrder* shared = nullptr) {
   pkd_status st = check_run(plan, q, k_cache, v_cache, page_stride, o, workspace,
                             workspace_bytes);
   if (st != PKD_OK) return st;
@@ -546,12 +578,20 @@ pkd_status run_impl(const pkd_plan* plan, const void* q, const void* k_cache,
     if (e != hipSuccess) return hip_fail((hipError_t)e, "decode launch");
     return PKD_OK;
   }
-  std::lock_guard<std::mutex> lock(plan->run_mu);
-  pkd_status busy = check_not_in_flight(plan, hs, "pkd_run");
-  if (busy != PKD_OK) return busy;
+  // (locks in a fixed order: the plan's, then the shared state's)
+  std::lock_guard<std::mutex> lock(plan->order.mu);
+  pkd_status ord = order_after(plan->order, hs, "ordering the run after the plan's last run");
+  if (ord != PKD_OK) return ord;
+  std::unique_lock<std::mutex> lock_shared;
+  if (shared != nullptr) {
+    lock_shared = std::unique_lock<std::mutex>(shared->mu);
+    ord = order_after(*shared, hs, "ordering the run after the last use of the static workspace");
+    if (ord != PKD_OK) return ord;
+  }
   int e = pkd::launch_decode(p, a, plan->host.info.num_workgroups, stream);
   if (e != hipSuccess) return hip_fail((hipError_t)e, "decode launch");
-  note_run(plan, hs);
+  note_launch(plan->order, hs);
+  if (shared != nullptr) note_launch(*shared, hs);
   return PKD_OK;
 }
 
@@ -591,8 +631,9 @@ pkd_status pkd_run_static_workspace(const pkd_plan* plan, const void* q, const v
   if (ws == nullptr)
     return pkd::fail(PKD_EHIP, "the static workspace's device address could not be "
                                "looked up on device " + std::to_string(dev));
+  RunOrder* shared = dev < kMaxDevices ? &g_static_order[dev] : nullptr;
   return run_impl(plan, q, k_cache, v_cache, page_stride, q_scale, k_scale, v_scale, sinks,
-                  o, lse, ws, pkd::kStaticScratchBytes, stream);
+                  o, lse, ws, pkd::kStaticScratchBytes, stream, shared);
 }
 
 pkd_status pkd_merge_states(const float* v, const float* s, int32_t rows,

@@ -1,7 +1,11 @@
-"""Runs of one plan on two streams (GPU). The workgroups of a run share the
-plan's work counters, so a run on a second stream while the first is still
-in flight must be refused (PKD_EBUSY), and accepted once it has finished.
-Every test prints its case before it touches the GPU."""
+"""Runs that share device state, on two streams (GPU). The workgroups of a
+run share the plan's work counters, and calls of pkd_run_static_workspace
+share the GPU's static workspace, so the library orders such a run after the
+previous one when it goes to another stream: the second stream waits on the
+GPU, with no host synchronisation. Checked on the GPU's own timeline: with
+the first stream kept busy for milliseconds, the second run, although its
+stream is idle, finishes after the first. Every test prints its case before
+it touches the GPU."""
 import pytest
 import torch
 
@@ -25,33 +29,61 @@ def keep_busy(stream):
     return a
 
 
-def test_run_on_a_second_stream_while_the_first_is_in_flight_is_refused():
-    w = wl.small_workload(seed=71, batch=6, num_qo_heads=32, num_kv_heads=8, head_dim=128,
-                          lengths=("fixed", [3000, 17, 900, 4096, 1, 2500]))
-    say(w)
-    case = wl.make_case(w, device="cuda")
-    plan = plan_for(w, case)
-    ws = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
-    ref = plan.run(case.q, case.pool, workspace=ws)
-    torch.cuda.synchronize()
+def ordered(first_run, second_run):
+    """Runs first_run on a busy stream s1, then at once second_run on an idle
+    stream s2; returns the milliseconds from the end of the first to the end
+    of the second on the GPU's clock."""
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
     s1.wait_stream(torch.cuda.current_stream())
     s2.wait_stream(torch.cuda.current_stream())
+    e1, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     busy = keep_busy(s1)
-    o1 = torch.empty_like(ref)
-    plan.run(case.q, case.pool, out=o1, workspace=ws, stream=s1)   # queued behind it
-    with pytest.raises(pkd.PkdError) as e:
-        plan.run(case.q, case.pool, workspace=ws, stream=s2)
-    assert e.value.status == pkd.PKD_EBUSY
-    # the same stream again is ordered after the first run: accepted
-    o1b = torch.empty_like(ref)
-    plan.run(case.q, case.pool, out=o1b, workspace=ws, stream=s1)
-    s1.synchronize()
-    o2 = torch.empty_like(ref)
-    plan.run(case.q, case.pool, out=o2, workspace=ws, stream=s2)
-    s2.synchronize()
-    assert torch.equal(o1, ref) and torch.equal(o1b, ref) and torch.equal(o2, ref)
+    first_run(s1)
+    e1.record(s1)
+    second_run(s2)
+    e2.record(s2)
+    torch.cuda.synchronize()
     del busy
+    return e1.elapsed_time(e2)
+
+
+def workload(seed):
+    return wl.small_workload(seed=seed, batch=6, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                             lengths=("fixed", [3000, 17, 900, 4096, 1, 2500]),
+                             fixed_split_size=16)
+
+
+def test_runs_of_one_plan_on_two_streams_are_ordered():
+    w = workload(71)
+    say(w)
+    case = wl.make_case(w, device="cuda")
+    plan = plan_for(w, case)
+    ws1 = torch.empty(max(plan.workspace_bytes, 256), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty_like(ws1)
+    ref = plan.run(case.q, case.pool, workspace=ws1)
+    torch.cuda.synchronize()
+    o1, o2 = torch.empty_like(ref), torch.empty_like(ref)
+    gap = ordered(lambda s: plan.run(case.q, case.pool, out=o1, workspace=ws1, stream=s),
+                  lambda s: plan.run(case.q, case.pool, out=o2, workspace=ws2, stream=s))
+    say("second run ends", gap, "ms after the first")
+    assert gap > 0
+    assert torch.equal(o1, ref) and torch.equal(o2, ref)
+
+
+def test_static_workspace_runs_of_two_plans_on_two_streams_are_ordered():
+    wa, wb = workload(75), workload(76)
+    say(wa, wb)
+    ca, cb = wl.make_case(wa, device="cuda"), wl.make_case(wb, device="cuda")
+    pa, pb = plan_for(wa, ca), plan_for(wb, cb)
+    assert pa.workspace_bytes > 0 and pb.workspace_bytes > 0
+    ra, rb = pa.run(ca.q, ca.pool), pb.run(cb.q, cb.pool)
+    torch.cuda.synchronize()
+    oa, ob = torch.empty_like(ra), torch.empty_like(rb)
+    gap = ordered(lambda s: pa.run_static_workspace(ca.q, ca.pool, out=oa, stream=s),
+                  lambda s: pb.run_static_workspace(cb.q, cb.pool, out=ob, stream=s))
+    say("second run ends", gap, "ms after the first")
+    assert gap > 0
+    assert torch.equal(oa, ra) and torch.equal(ob, rb)
 
 
 def test_temporaries_of_a_run_on_a_side_stream_stay_valid():
