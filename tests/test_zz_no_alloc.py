@@ -73,3 +73,40 @@ def test_static_workspace_refuses_a_plan_that_needs_more():
     with pytest.raises(pkd.PkdError) as e:
         plan.run_static_workspace(case.q, case.pool)
     assert e.value.status == pkd.PKD_EWORKSPACE and "static workspace" in str(e.value)
+
+
+def test_static_workspace_run_captured_in_a_graph():
+    """The caller it is for: a run recorded into a HIP graph. Two calls (two
+    queries) are captured; every replay, with eager static-workspace calls,
+    output clears and synchronisations between replays, gives the eager
+    bits."""
+    w = wl.small_workload(seed=87, batch=6, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                          q_dtype="bf16", kv_dtype="bf16", o_dtype="bf16", layout="HND",
+                          lengths=("fixed", [5000, 70, 12000, 4096, 1, 3000]),
+                          fixed_split_size=16)
+    say(w, "graph")
+    case = wl.make_case(w, device="cuda")
+    plan = plan_for(w, case)
+    assert plan.workspace_bytes > 0
+    q2 = torch.flip(case.q, dims=[0]).contiguous()
+    ref = []
+    for q in (case.q, q2):
+        o, lse = plan.run_static_workspace(q, case.pool, return_lse=True)
+        ref.append((o.clone(), lse.clone()))
+    torch.cuda.synchronize()
+    outs = [(torch.empty_like(r[0]), torch.empty_like(r[1])) for r in ref]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for q, (o, lse) in zip((case.q, q2), outs):
+            plan.run_static_workspace(q, case.pool, out=o, lse=lse)
+    for rep in range(4):
+        for o, lse in outs:
+            o.zero_()
+            lse.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        for (o, lse), (ro, rl) in zip(outs, ref):
+            assert torch.equal(o, ro) and torch.equal(lse, rl), rep
+        eo, el = plan.run_static_workspace(q2, case.pool, return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(eo, ref[1][0]) and torch.equal(el, ref[1][1]), rep
