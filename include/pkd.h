@@ -295,8 +295,10 @@ void pkd_plan_destroy(pkd_plan* plan);
  * runs of one plan must be ordered by the caller.
  * Alignment: q, k_cache, v_cache 16 bytes (and page_stride a multiple of 16
  * bytes), o 8 bytes, workspace 256 bytes.
+ * The stream must be on the plan's device (the current device for NULL).
  * Errors: PKD_EINVAL (null pointer, page_stride too small, misaligned
- * buffer), PKD_EWORKSPACE, PKD_EHIP (launch failure). */
+ * buffer, a stream of another device), PKD_EWORKSPACE, PKD_EHIP (launch
+ * failure). */
 pkd_status pkd_run(const pkd_plan* plan, const void* q, const void* k_cache,
                    const void* v_cache, int64_t page_stride, float q_scale,
                    float k_scale, float v_scale, const float* sinks, void* o,

@@ -519,6 +519,18 @@ pkd_status run_impl(const pkd_plan* plan, const void* q, const void* k_cache,
   if (plan->item_capacity() == 0) return PKD_OK;
   if (!std::isfinite(q_scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return pkd::fail(PKD_EINVAL, "q_scale, k_scale and v_scale must be finite");
+  {
+    // the kernel runs on the stream's device (the current one for the null
+    // stream) and reads the plan's memory, which lives on the plan's device
+    int dev = -1;
+    const hipError_t e = stream != nullptr
+                             ? hipStreamGetDevice(reinterpret_cast<hipStream_t>(stream), &dev)
+                             : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "querying the stream's device");
+    if (dev != plan->device)
+      return pkd::fail(PKD_EINVAL, "the run's stream is on device " + std::to_string(dev) +
+                                       ", the plan on device " + std::to_string(plan->device));
+  }
   pkd::DecodeArgs a{};
   a.counters = plan->d_counters();
   a.reserve = plan->d_reserve();
