@@ -26,7 +26,9 @@ kv head) + q + o + fp32 lse + the page indices of the touched pages + indptr
 + last_page_len. ``roofline`` is that kernel, timed with HIP events on the
 stream it runs on, around each timed region. ``cpu_baseline`` times the fp64 CPU oracle on a bounded
 sample: the median of three runs over the same requests, and for the two
-small workloads also a run limited to one thread.
+small workloads also a run limited to one thread. ``per_call_events`` gives
+single calls timed with HIP events, median and p10/p90 of 100: "cold", each
+after an untimed 1 GiB fill that evicts the caches, and "hot", without it.
 """
 import argparse
 import hashlib
@@ -185,6 +187,33 @@ def profiled_traffic(workload: str, src_hash: str, launch_bytes: int):
     return float(t.group(1))
 
 
+def per_call_protocol(call, first, n, dev, warm=10, flush_bytes=1 << 30):
+    """Median / p10 / p90 µs of n single calls, each bracketed by HIP events
+    on the current stream: "cold" with an untimed fill of flush_bytes before
+    every call (more than the L2s and the 256 MB Infinity Cache hold), "hot"
+    with no fill and the same pool every call. The fill keeps the GPU busy
+    between calls, so the clocks stay up."""
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device=dev)
+    out = {"calls": n, "warmup_calls": warm, "flush_bytes": flush_bytes}
+    for label, flush in (("cold", True), ("hot", False)):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n)]
+        for i in range(warm + n):
+            if flush:
+                scratch.fill_(i & 0xFF)
+            # hot: call `first` on its pool every time; cold: rotate as usual
+            k = first + i if flush else first
+            call(k, evs[i - warm] if i >= warm else None)
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        out[label] = {"median_us": round(float(np.median(us)), 2),
+                      "p10_us": round(float(np.percentile(us, 10)), 2),
+                      "p90_us": round(float(np.percentile(us, 90)), 2)}
+    del scratch
+    torch.cuda.synchronize()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +228,9 @@ def main():
                          "32 for the class example, whose loop runs over 32 "
                          "layers, else 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-calls", type=int, default=100,
+                    help="single calls timed with HIP events, each after an untimed "
+                         "1 GiB cache-evicting fill (and as many without it); 0 skips")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device copy (for counter scaling)")
     ap.add_argument("--eager", action="store_true",
@@ -269,6 +301,12 @@ def main():
     for k in range(base):
         call(k)
     torch.cuda.synchronize()
+    # Per-call protocol: HIP events around each single call, every call
+    # preceded by an untimed 1 GiB fill that evicts the L2 and the Infinity
+    # Cache ("cold"), and the same without the fill on one pool ("hot").
+    # Taken before the graph so that the graph's replays stay the last
+    # launches of a run.
+    flushed = per_call_protocol(call, base, args.flush_calls, dev) if args.flush_calls > 0 else None
     # Eager pass: K steps launched from the host (the eager per-call figure).
     t0 = time.perf_counter()
     for k in range(calls):
@@ -394,6 +432,7 @@ def main():
             "kernel_source_hash": src_hash,
         },
         "cpu_baseline": cpu,
+        "per_call_events": flushed,
     }
     print(json.dumps(line), flush=True)
 
