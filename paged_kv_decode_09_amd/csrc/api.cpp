@@ -264,28 +264,6 @@ pkd_status query_plan(const pkd_plan_params* params, const int32_t* indptr,
   return PKD_OK;
 }
 
-// Capacities of a graph plan for B requests holding at most max_pages pages
-// in all: units per kv head (all requests, and one request) from the
-// planner's rules (at most one unit per started chunk and sub-chunk under a
-// fixed split; units of at least kUnitQuantum tokens under its own split).
-void graph_capacities(const pkd_plan_params& p, int32_t max_pages, int64_t* units_total,
-                      int64_t* units_one) {
-  const int64_t B = p.batch_size, P = p.page_size, M = max_pages;
-  if (p.disable_split_kv) {
-    *units_total = B;
-    *units_one = 1;
-  } else if (p.fixed_split_size > 0) {
-    const int64_t S = p.fixed_split_size;
-    const int64_t cap = std::min<int64_t>(S * P, pkd::kFixedUnitMaxTokens);
-    const int64_t sub = (S * P + cap - 1) / cap;
-    *units_total = (M / S + B) * sub;
-    *units_one = (M / S + 1) * sub;
-  } else {
-    *units_total = M * P / pkd::kUnitQuantumTokens + B;
-    *units_one = M * P / pkd::kUnitQuantumTokens + 1;
-  }
-}
-
 pkd_status create_plan(const pkd_plan_params* params, const int32_t* indptr,
                        const int32_t* last_page_len, const int32_t* page_base,
                        const int32_t* indices, void* stream, pkd_plan** out,
@@ -322,7 +300,7 @@ pkd_status create_plan(const pkd_plan_params* params, const int32_t* indptr,
   (void)pkd::static_scratch_resolve(dev);
   if (graph_max_pages > 0) {
     int64_t total = 0, one = 0;
-    graph_capacities(*params, graph_max_pages, &total, &one);
+    pkd::graph_capacities(*params, graph_max_pages, p->slots, &total, &one);
     const int64_t items = total * params->num_kv_heads;
     const int64_t stride = 1 + (one + pkd::kMergeGroup - 1) / pkd::kMergeGroup;
     const int32_t Q = pkd::q_len_of(*params);

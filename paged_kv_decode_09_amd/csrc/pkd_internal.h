@@ -19,8 +19,10 @@ constexpr int kStepTokens = 32;
 constexpr int kMaxGroup = 16;       // query rows per kv head: G * Q (one MFMA tile)
 constexpr int kMergeRowsPerBlock = 4;
 // Units the planner sizes itself are multiples of kUnitQuantumTokens tokens
-// (two 32-token steps for each wavefront) and never shorter; under a fixed
-// split, chunks are processed as units of at most kFixedUnitMaxTokens tokens.
+// (two 32-token steps for each wavefront) and never shorter, unless the batch
+// is too small to give every workgroup such a unit (then multiples of one
+// step for each wavefront); under a fixed split, chunks are processed as
+// units of at most kFixedUnitMaxTokens tokens.
 constexpr int kUnitQuantumTokens = 2 * kWaves * kStepTokens;
 constexpr int kFixedUnitMaxTokens = 3072;
 // Units of a split request are merged in two levels: each run of
@@ -105,6 +107,12 @@ pkd_status block_table_csr(const pkd_plan_params& p, const int32_t* seq_lens,
                            int32_t max_blocks, std::vector<int32_t>* indptr,
                            std::vector<int32_t>* last_page_len,
                            std::vector<int32_t>* page_base);
+
+// Capacities of a graph plan for p.batch_size requests holding at most
+// max_pages pages in all, on a launch of `slots` workgroups: the most units
+// per kv head the planner can make (all requests, and one request).
+void graph_capacities(const pkd_plan_params& p, int32_t max_pages, int64_t slots,
+                      int64_t* units_total, int64_t* units_one);
 
 // Decode workgroups per compute unit the kernel instance of `p` is built for.
 int32_t decode_wgs_per_cu_table(const pkd_plan_params& p);

@@ -57,8 +57,11 @@ constexpr int kSplitRowsRef = 4;
 // for each wavefront of a workgroup, so that every wavefront runs an even
 // number of steps (its loop takes steps in pairs).
 constexpr int kUnitQuantum = kUnitQuantumTokens;
-// Smallest unit the planner creates on its own, in tokens.
+// Smallest unit the planner creates on its own, in tokens, except for a batch
+// too small to fill the workgroups with such units: there the quantum is one
+// step for each wavefront.
 constexpr int kMinUnitTokens = kUnitQuantum;
+constexpr int kSmallUnitQuantum = kWaves * kStepTokens;
 // Under a fixed split, chunks longer than this are processed as sub-chunks of
 // this many tokens (cut at fixed offsets from the chunk start), so that the
 // work can be spread over all workgroups. The cut depends only on the
@@ -245,6 +248,10 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
   const int64_t slots = std::max<int64_t>(1, num_slots);
   int32_t split = 0;
   int64_t unit_cap = INT64_MAX;
+  // the units are the split's chunks on the grid of multiples of the chunk
+  // (a fixed split, and the planner's split of a small batch), else equal
+  // pieces of each request
+  bool grid = p.fixed_split_size > 0;
   if (p.disable_split_kv) {
     split = 0;
   } else if (p.fixed_split_size > 0) {
@@ -259,9 +266,25 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
                                  std::max<int64_t>(kSplitRowsRef, rows));
     {
       const int64_t total = attended * p.num_kv_heads;
-      int64_t unit = std::max<int64_t>(kMinUnitTokens, (total + units_wanted - 1) / units_wanted);
-      // an even number of steps for every wavefront of the workgroup
-      unit = (unit + kUnitQuantum - 1) / kUnitQuantum * kUnitQuantum;
+      int64_t quantum = kUnitQuantum, unit;
+      if (total <= slots * kUnitQuantum) {
+        // A batch too small to give every workgroup a unit of the usual
+        // quantum (a launch-bound call: the time is a chain of dependent
+        // memory round trips): units of one step per wavefront, no more of
+        // them than workgroups, so that as many compute units as possible
+        // stream their share at once, cut as a fixed split cuts (whole
+        // chunks and a remainder). (The class example's batch, 32 layers:
+        // 11.8 us per call with 160 such units; 12.2 us with 160 equal pieces
+        // or 96 of at most 256 tokens; 19.5 us with units of 64 tokens, more
+        // than the workgroups.)
+        quantum = kSmallUnitQuantum;
+        unit = std::max<int64_t>(quantum, (total + slots - 1) / slots);
+        grid = true;
+      } else {
+        unit = std::max<int64_t>(kMinUnitTokens, (total + units_wanted - 1) / units_wanted);
+      }
+      // (with the usual quantum, an even number of steps for every wavefront)
+      unit = (unit + quantum - 1) / quantum * quantum;
       int64_t pages_per_unit = (unit + P - 1) / P;
       split = pages_per_unit >= max_pages ? 0 : (int32_t)pages_per_unit;
     }
@@ -286,15 +309,33 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
     std::vector<std::pair<int64_t, int64_t>> ranges;
     if (split <= 0) {
       ranges.emplace_back(r.start, r.kv_len);
-    } else if (p.fixed_split_size <= 0) {
+    } else if (!grid) {
       // the planner's own split: the attended tokens in the fewest units of
       // at most `split` pages, all of about the same length (units that
       // differ less leave less for the longest-first order to even out)
       const int64_t att = r.kv_len - r.start;
       const int64_t cap = (int64_t)split * P;
       const int64_t n = (att + cap - 1) / cap;
-      for (int64_t c = 0; c < n; ++c)
-        ranges.emplace_back(r.start + att * c / n, r.start + att * (c + 1) / n);
+      // The cuts go to the nearest multiple of the kernel's step (steps start
+      // at multiples of kStepTokens): a cut inside a step would have both
+      // units load that step's rows. Should that make a unit longer than the
+      // cap (or empty), the request keeps the exact cuts.
+      std::vector<int64_t> cut(n + 1);
+      cut[0] = r.start;
+      cut[n] = r.kv_len;
+      bool aligned = true;
+      for (int64_t c = 1; c < n; ++c) {
+        const int64_t e = r.start + att * c / n;
+        cut[c] = (e + kStepTokens / 2) / kStepTokens * kStepTokens;
+      }
+      for (int64_t c = 0; c < n && aligned; ++c)
+        aligned = cut[c + 1] > cut[c] && cut[c + 1] - cut[c] <= cap;
+      for (int64_t c = 0; c < n; ++c) {
+        if (aligned)
+          ranges.emplace_back(cut[c], cut[c + 1]);
+        else
+          ranges.emplace_back(r.start + att * c / n, r.start + att * (c + 1) / n);
+      }
     } else {
       const int64_t chunk_tokens = (int64_t)split * P;
       const int64_t first = (r.start / P) / split;
@@ -386,5 +427,37 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
   clear_error();
   return PKD_OK;
 }
+
+// Capacities of a graph plan for B requests holding at most max_pages pages
+// in all: units per kv head (all requests, and one request) from the
+// planner's rules (at most one unit per started chunk and sub-chunk under a
+// fixed split). Under its own split the units are of at least kUnitQuantum
+// tokens, beyond one per request, or, for a batch of at most
+// slots * kUnitQuantum tokens over all kv heads, chunks of at least half that
+// on the chunk grid: at most 2 * slots / num_kv_heads of them per kv head,
+// beyond two per request.
+void graph_capacities(const pkd_plan_params& p, int32_t max_pages, int64_t slots,
+                      int64_t* units_total, int64_t* units_one) {
+  const int64_t B = p.batch_size, P = p.page_size, M = max_pages;
+  if (p.disable_split_kv) {
+    *units_total = B;
+    *units_one = 1;
+  } else if (p.fixed_split_size > 0) {
+    const int64_t S = p.fixed_split_size;
+    const int64_t cap = std::min<int64_t>(S * P, kFixedUnitMaxTokens);
+    const int64_t sub = (S * P + cap - 1) / cap;
+    *units_total = (M / S + B) * sub;
+    *units_one = (M / S + 1) * sub;
+  } else {
+    // (a small batch's units are chunks on the grid: a request's first one
+    // may start inside a chunk, one more unit per request)
+    const int64_t small = std::min<int64_t>(M * P / (kUnitQuantumTokens / 2),
+                                            2 * slots / std::max(1, p.num_kv_heads));
+    const int64_t full = M * P / kUnitQuantumTokens;
+    *units_total = std::max(full + B, small + 2 * B);
+    *units_one = std::max(full + 1, small + 2);
+  }
+}
+
 
 }  // namespace pkd

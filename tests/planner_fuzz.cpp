@@ -4,7 +4,8 @@
 // invalid; for every accepted plan it checks what the decode kernel relies
 // on: the units of each (request, kv head) tile the attended tokens
 // [start, kv_len) in chunk order, workspace slots are distinct and counted,
-// and every item field is in range. Prints "ok <plans> <rejected>" and exits
+// every item field is in range, and a graph plan whose capacity is the
+// table's page count would hold the plan. Prints "ok <plans> <rejected>" and exits
 // 0, or names the first violation and exits 1.
 #include <cstdio>
 #include <cstdlib>
@@ -138,6 +139,14 @@ int main(int argc, char** argv) {
       st = pkd::build_host_plan(p, indptr.data(), last.data(), slots, &h);
       if (st == PKD_OK) {
         if (check(p, indptr, last, h)) return fprintf(stderr, "iteration %d\n", n), 1;
+        // a graph plan with a capacity of this table's pages holds the plan
+        int64_t tot = 0, one = 0, most = 0;
+        pkd::graph_capacities(p, indptr[B], std::max(1, slots), &tot, &one);
+        for (const auto& it : h.items) most = std::max<int64_t>(most, it.num_chunks);
+        if ((int64_t)h.items.size() > tot * p.num_kv_heads || most > one)
+          return fprintf(stderr, "graph capacity %lld x %d heads / %lld below %zu items / %lld "
+                         "chunks (iteration %d)\n", (long long)tot, p.num_kv_heads,
+                         (long long)one, h.items.size(), (long long)most, n), 1;
         ++plans;
         continue;
       }

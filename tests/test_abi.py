@@ -144,16 +144,25 @@ def test_split_chunks_tile_each_request(split, window):
     per = coverage(items, 4, lens, starts)
     if split == 0:
         # the planner's split: each request in the fewest units of at most
-        # split_pages pages, of equal length to the token
+        # split_pages pages, of equal length to the token, with the cuts
+        # moved to the nearest multiple of 32 tokens (the kernel's step)
+        # unless that makes a unit longer than split_pages pages
         cap_t = info.split_pages * 16
+        # a batch too small to give each of the 256 workgroups 256 tokens is
+        # cut as a fixed split of split_pages cuts it
+        small = info.attended_tokens * 4 <= 256 * info.workgroups_per_cu * 256
 
         def bounds(L):
             s0 = oracle.window_start(L, window)
             if cap_t == 0:
                 return [(s0, L)]
+            if small:
+                return unit_bounds(L, 16, info.split_pages, window, FIXED_UNIT_MAX)
             n = -(-(L - s0) // cap_t)
-            return [(s0 + (L - s0) * c // n, s0 + (L - s0) * (c + 1) // n)
-                    for c in range(n)]
+            exact = [s0 + (L - s0) * c // n for c in range(n + 1)]
+            moved = [s0] + [(e + 16) // 32 * 32 for e in exact[1:-1]] + [L]
+            cuts = moved if all(0 < b - a <= cap_t for a, b in zip(moved, moved[1:])) else exact
+            return list(zip(cuts, cuts[1:]))
     else:
         assert info.split_pages == split
 
@@ -246,6 +255,23 @@ def test_auto_split_respects_minimum_unit():
     info, items = query([0, 1000], [16], num_qo_heads=64, num_kv_heads=8)
     assert info.split_pages * 16 >= 256     # two steps for each of 4 waves
     assert all(i.token_end - i.token_begin <= info.split_pages * 16 for i in items)
+
+
+def test_small_batch_units_of_one_step_per_wavefront():
+    # the class example's batch (64/8 heads, 1982 tokens): too small to give
+    # each of 256 workgroups a unit of 256 tokens, so the units are of at most
+    # 128 tokens (one 32-token step for each of the 4 wavefronts), no more of
+    # them than workgroups
+    w = wl.WORKLOADS["worked_example"]
+    pt = wl.make_page_table(w, np.random.default_rng(w.seed))
+    info, items = query(pt.indptr, pt.last_page_len, num_qo_heads=w.num_qo_heads,
+                        num_kv_heads=w.num_kv_heads)
+    assert info.split_pages * 16 == 128
+    sizes = [i.token_end - i.token_begin for i in items]
+    assert max(sizes) <= 128 and len(items) <= 256
+    # a batch that fills the workgroups keeps units of at least 256 tokens
+    info, items = query([0, 16 * 64], [16], num_qo_heads=64, num_kv_heads=64)
+    assert info.split_pages * 16 >= 256
 
 
 def test_empty_batch_plans_nothing():
