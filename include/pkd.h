@@ -102,8 +102,7 @@ typedef struct {
   int32_t pos_encoding_mode; /* pkd_pos_encoding. ROPE_LLAMA turns q at its
                                position L_i - Q + j and each key at its token
                                index (pairs d, d + head_dim/2); it is
-                               PKD_EUNSUPPORTED with head_dim 64 and E4M3
-                               keys, and for kv lengths above 2^24         */
+                               PKD_EUNSUPPORTED for kv lengths above 2^24  */
   float rope_scale;         /* ROPE_LLAMA: angle = pos / rope_scale *       */
   float rope_theta;         /* rope_theta^(-2d/head_dim); both positive and
                                finite (else PKD_EINVAL), unused otherwise   */

@@ -180,6 +180,30 @@ __device__ __forceinline__ float wave_sum_over_groups(float x) {
   return p[0] + p[1];
 }
 
+// Both results of gfx950's v_permlane32_swap on two copies of x: one lane's
+// pair holds x[l] and x[l ^ 32] (which is which depends on the lane's half;
+// swap_other() below picks the partner's). The copies are made opaque as in
+// lane_pair.
+__device__ __forceinline__ u32x2 swap_halves(unsigned x) {
+  unsigned a = x, b = x;
+  asm volatile("" : "+v"(a));
+  asm volatile("" : "+v"(b));
+  auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  const unsigned r0 = r[0], r1 = r[1];
+  return (u32x2){r0, r1};
+}
+// x of lane l ^ 32. `second` (from partner_slot) says which result of the
+// exchange holds it in this lane.
+__device__ __forceinline__ unsigned swap_other(unsigned x, bool second) {
+  const u32x2 r = swap_halves(x);
+  return second ? r[1] : r[0];
+}
+// Whether the second result of the exchange holds lane l ^ 32's value in
+// lane l: found by exchanging the lane index itself (once per kernel).
+__device__ __forceinline__ bool partner_slot(unsigned lane) {
+  return swap_halves(lane)[1] == (lane ^ 32u);
+}
+
 // Device-scope (agent) relaxed atomic store: it bypasses the caches that are
 // not coherent across the XCDs, so a workgroup on any XCD that loads with
 // the sc1 policy (load_coherent4/1 below) sees the value once the storing
@@ -570,6 +594,32 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
   // halves (d, d + HD/2) of the same rotary pairs, so each lane turns its
   // own elements. Element e of piece j is hd index qk_hd(j, g) + e.
   constexpr int kHalf = G_::kQkMfma / 2;
+  // Head_dim 64 with E4M3 keys: lane group g holds dims 16g..16g+15 of its
+  // row (both operand pieces), so the partner d +- 32 of each of its dims
+  // sits in lane l ^ 32 (group g ^ 2). The lanes exchange their pieces with
+  // gfx950's half-wave swap and each turns its own 16 elements: with c, s of
+  // pair d mod 32, a first-half element becomes own * c - partner * s, a
+  // second-half one own * c + partner * s.
+  constexpr bool kRopeCross = ROPE && KV8 && HD == 64;
+  [[maybe_unused]] const bool swap_second = kRopeCross ? partner_slot((unsigned)lane) : false;
+  [[maybe_unused]] const float rope_sgn = g >= 2 ? 1.0f : -1.0f;
+  // q of this column at its query position (kRopeCross)
+  auto rope_q_cross = [&](int pos) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const u32x4 w = __builtin_bit_cast(u32x4, bq[j]);
+      u32x4 pw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[i] = swap_other(w[i], swap_second);
+      const v8 par = __builtin_bit_cast(v8, pw);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float c, sn;
+        rope_cos_sin(pos, s_rope[16 * (g & 1) + 8 * j + e], c, sn);
+        bq[j][e] = (typename O::et)((float)bq[j][e] * c + rope_sgn * (float)par[e] * sn);
+      }
+    }
+  };
   auto rope_pair = [&](v8& lo_op, v8& hi_op, int j, int pos) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -630,8 +680,12 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
       // q at its query position, once per unit (its loads have landed by
       // the unit's first step)
       if (!q_turned) {
+        if constexpr (kRopeCross) {
+          rope_q_cross(col_hi);
+        } else {
 #pragma unroll
-        for (int j = 0; j < kHalf; ++j) rope_pair(bq[j], bq[j + kHalf], j, col_hi);
+          for (int j = 0; j < kHalf; ++j) rope_pair(bq[j], bq[j + kHalf], j, col_hi);
+        }
         q_turned = true;
       }
     }
@@ -646,6 +700,53 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
       const int tok = t0 + tau0;
       sc[0] = (f32x4){0.f, 0.f, 0.f, 0.f};
       sc[1] = sc[0];
+      if constexpr (kRopeCross) {
+        // the partner lane's 16 E4M3 codes of the same row, then each own
+        // element turned with its pair's angle (tile 1's from tile 0's)
+        u32x4 own[2], par[2];
+#pragma unroll
+        for (int tile = 0; tile < 2; ++tile) {
+          own[tile] = kr[tile][0];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) par[tile][i] = swap_other(own[tile][i], swap_second);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          u32x4 k0, k1;   // the rotated pieces j of tiles 0 and 1, packed
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            // elements 8j + 2q, 8j + 2q + 1: word 2j + q / 2, half q % 2
+            const int wi = 2 * j + (q >> 1);
+            f32x2 o0, p0, o1, p1;
+            if (q & 1) {
+              o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(own[0][wi], 1.0f, true);
+              p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(par[0][wi], 1.0f, true);
+              o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(own[1][wi], 1.0f, true);
+              p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(par[1][wi], 1.0f, true);
+            } else {
+              o0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(own[0][wi], 1.0f, false);
+              p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(par[0][wi], 1.0f, false);
+              o1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(own[1][wi], 1.0f, false);
+              p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(par[1][wi], 1.0f, false);
+            }
+            float r0[2], r1[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int i = 16 * (g & 1) + 8 * j + 2 * q + u;   // pair index
+              float c0, s0;
+              rope_cos_sin(tok, s_rope[i], c0, s0);
+              const f32x2 r4 = s_rope4[i];
+              const float c1 = c0 * r4[0] - s0 * r4[1], s1 = s0 * r4[0] + c0 * r4[1];
+              r0[u] = o0[u] * c0 + rope_sgn * p0[u] * s0;
+              r1[u] = o1[u] * c1 + rope_sgn * p1[u] * s1;
+            }
+            k0[q] = O::pack(r0[0], r0[1]);
+            k1[q] = O::pack(r1[0], r1[1]);
+          }
+          sc[0] = O::mfma(__builtin_bit_cast(v8, k0), bq[j], sc[0]);
+          sc[1] = O::mfma(__builtin_bit_cast(v8, k1), bq[j], sc[1]);
+        }
+      } else {
 #pragma unroll
       for (int j = 0; j < kHalf; ++j) {
         if constexpr (kPieceByPiece) {
@@ -676,6 +777,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
         sc[0] = O::mfma(hi0, bq[j + kHalf], sc[0]);
         sc[1] = O::mfma(lo1, bq[j], sc[1]);
         sc[1] = O::mfma(hi1, bq[j + kHalf], sc[1]);
+      }
       }
     } else {
 #pragma unroll

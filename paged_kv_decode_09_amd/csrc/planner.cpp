@@ -104,10 +104,6 @@ pkd_status check_params(const pkd_plan_params& p) {
         !std::isfinite(p.rope_theta))
       return fail(PKD_EINVAL, fmt("rope_scale %g and rope_theta %g must be positive and finite",
                                   p.rope_scale, p.rope_theta));
-    // each lane rotates pairs (d, d + head_dim/2) it holds itself; with
-    // head_dim 64 and E4M3 keys the two halves sit in different lanes
-    if (p.head_dim == 64 && p.kv_dtype == PKD_E4M3)
-      return fail(PKD_EUNSUPPORTED, "ROPE_LLAMA with head_dim 64 and E4M3 keys is not built");
   }
   if (p.pos_encoding_mode != PKD_POS_NONE && p.pos_encoding_mode != PKD_POS_ALIBI &&
       p.pos_encoding_mode != PKD_POS_ROPE_LLAMA)

@@ -59,7 +59,6 @@ def query(indptr, last, num_cus=256, **kw):
     (dict(q_data_type="float16", kv_data_type="bfloat16"), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "kv_dtype"),
     (dict(o_data_type="float8_e4m3fn"), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "o_dtype"),
     (dict(q_len_per_req=-1), [0, 1], [1], pkd.PKD_EINVAL, "q_len_per_req -1"),
-    (dict(pos_encoding_mode="ROPE_LLAMA", head_dim=64, kv_data_type="float8_e4m3fn"), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "head_dim 64 and E4M3"),
     (dict(pos_encoding_mode="ROPE_LLAMA", rope_theta=-1.0), [0, 1], [1], pkd.PKD_EINVAL, "must be positive"),
     (dict(pos_encoding_mode="XPOS"), [0, 1], [1], pkd.PKD_EINVAL, "pos_encoding_mode -1"),
     (dict(q_len_per_req=5), [0, 1], [8], pkd.PKD_EUNSUPPORTED, "group size 4 x q_len_per_req 5"),

@@ -55,7 +55,8 @@ def check_rope_lse(w, case, reqs, lse_gpu, ref_l, theta, scale):
 @pytest.mark.parametrize("hd,kv,Q,cap,window,layout", [
     (128, "bf16", 1, 0.0, -1, "NHD"), (128, "f16", 3, 0.0, -1, "HND"),
     (64, "f16", 1, 0.0, 40, "HND"), (256, "bf16", 1, 30.0, -1, "NHD"),
-    (128, "e4m3", 2, 0.0, -1, "NHD"), (256, "e4m3", 1, 0.0, 100, "HND")])
+    (128, "e4m3", 2, 0.0, -1, "NHD"), (256, "e4m3", 1, 0.0, 100, "HND"),
+    (64, "e4m3", 1, 0.0, -1, "NHD"), (64, "e4m3", 2, 30.0, 50, "HND")])
 @pytest.mark.parametrize("theta,scale", [(1e4, 1.0), (5e5, 8.0)])
 @pytest.mark.parametrize("split", [None, 3])
 def test_rope_matches_oracle(hd, kv, Q, cap, window, layout, theta, scale, split):
