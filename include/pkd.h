@@ -85,7 +85,7 @@ typedef enum { PKD_POS_NONE = 0, PKD_POS_ROPE_LLAMA = 1, PKD_POS_ALIBI = 2 } pkd
 typedef struct {
   int32_t batch_size;       /* B >= 0                                       */
   int32_t num_qo_heads;     /* >= 1, a multiple of num_kv_heads             */
-  int32_t num_kv_heads;     /* >= 1; G = num_qo_heads/num_kv_heads <= 16    */
+  int32_t num_kv_heads;     /* >= 1; G = num_qo_heads/num_kv_heads, any    */
   int32_t head_dim;         /* 64, 128 or 256                               */
   int32_t page_size;        /* a power of two, 1 .. 256                     */
   int32_t layout;           /* pkd_layout                                   */
@@ -98,7 +98,7 @@ typedef struct {
   int32_t fixed_split_size; /* pages per chunk; 0: the planner chooses      */
   int32_t disable_split_kv; /* nonzero: exactly one chunk per request       */
   int32_t q_len_per_req;    /* Q, query tokens per request; 0 means 1;
-                               G*Q <= 16 and every L_i >= Q                 */
+                               Q <= 16 and every L_i >= Q                   */
   int32_t pos_encoding_mode; /* pkd_pos_encoding. ROPE_LLAMA turns q at its
                                position L_i - Q + j and each key at its token
                                index (pairs d, d + head_dim/2); it is
@@ -109,13 +109,23 @@ typedef struct {
 } pkd_plan_params;
 
 /* One unit of decode work: the tokens [token_begin, token_end) of one chunk of
- * one request, for one kv head and its G q heads (and the Q query tokens).
+ * one request, for one kv head and its G q heads, or a block of them (below),
+ * and the Q query tokens.
  * Tokens past a query token's position, or before its window, are masked
  * for that token only. Under a fixed split, chunks
  * longer than 3072 tokens are processed as units of 3072 tokens cut at fixed
  * offsets from the chunk start, so each unit depends on its request alone.
  * Under the planner's own split a request is cut into units of equal length
- * (to the token), as few as keep each within split_pages pages. */
+ * (to the token, the cuts then moved to multiples of 32 tokens unless a unit
+ * would pass the cap), as few as keep each within split_pages pages; a batch
+ * too small to give every workgroup 256 tokens is cut as a fixed split of
+ * split_pages would cut it.
+ * A unit carries at most 16 query rows (G*Q). A larger group is split into
+ * the fewest nb equal blocks of G/nb q heads with (G/nb)*Q <= 16, and
+ * kv_head then numbers blocks: block b of kv head h is kv_head h*nb + b, it
+ * covers q heads (h*nb + b)*(G/nb) .. + G/nb - 1 and reads kv head h's K/V
+ * (each block reads it once; a group with no divisor that fits runs one q
+ * head per block). */
 typedef struct {
   int32_t request;
   int32_t kv_head;
@@ -124,7 +134,7 @@ typedef struct {
   int32_t page_base;        /* indptr[request] (block table: request*row)   */
   int32_t partial;          /* -1: writes o/lse; else its workspace slot    */
   int32_t chunk;            /* unit index within the request (ascending)    */
-  int32_t num_chunks;       /* units of the request per kv head (1: unsplit) */
+  int32_t num_chunks;       /* units of the request per kv_head (1: unsplit) */
   int32_t query_pos;        /* position of the request's first query token,
                                L_i - Q                                      */
 } pkd_work_item;

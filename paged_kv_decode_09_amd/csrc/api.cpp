@@ -60,7 +60,8 @@ struct pkd_plan {
   }
   size_t merge_counter_bytes() const {
     const size_t n =
-        (size_t)host.params.batch_size * host.params.num_kv_heads * merge_stride() * 4;
+        (size_t)host.params.batch_size * host.params.num_kv_heads * host.kv_blocks *
+            merge_stride() * 4;
     return (n + 63) & ~(size_t)63;
   }
   size_t reserve_bytes() const {
@@ -301,11 +302,12 @@ pkd_status create_plan(const pkd_plan_params* params, const int32_t* indptr,
   if (graph_max_pages > 0) {
     int64_t total = 0, one = 0;
     pkd::graph_capacities(*params, graph_max_pages, p->slots, &total, &one);
-    const int64_t items = total * params->num_kv_heads;
+    const int64_t heads = (int64_t)params->num_kv_heads * pkd::kv_blocks(*params);
+    const int64_t items = total * heads;
     const int64_t stride = 1 + (one + pkd::kMergeGroup - 1) / pkd::kMergeGroup;
     const int32_t Q = pkd::q_len_of(*params);
     if (items >= (int64_t)pkd::kMaxItems ||
-        (int64_t)params->batch_size * params->num_kv_heads * stride * 4 > INT32_MAX / 2 ||
+        (int64_t)params->batch_size * heads * stride * 4 > INT32_MAX / 2 ||
         total * Q * params->num_qo_heads * params->head_dim * 4 > INT32_MAX) {
       delete p;
       return pkd::fail(PKD_EUNSUPPORTED, "graph plan capacity of " +
@@ -539,8 +541,9 @@ pkd_status run_impl(const pkd_plan* plan, const void* q, const void* k_cache,
     a.head_stride = p.page_size * p.head_dim;
   }
   a.num_qo_heads = p.num_qo_heads;
-  a.num_kv_heads = p.num_kv_heads;
-  a.group = p.num_qo_heads / p.num_kv_heads;
+  a.kv_div = plan->host.kv_blocks;
+  a.num_kv_heads = p.num_kv_heads * a.kv_div;
+  a.group = p.num_qo_heads / a.num_kv_heads;
   a.q_len = Q;
   a.cols = a.group * Q;
   a.window_left = p.window_left;

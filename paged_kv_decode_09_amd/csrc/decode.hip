@@ -478,6 +478,9 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
   const int n = lane & 15;        // MFMA row (tile token) / column (q head)
   const int g = lane >> 4;        // lane group
   const int group = a.group;
+  // the cache's kv head of an item head (a block of its q heads when the
+  // group is split; the division is skipped otherwise)
+  auto cache_head = [&](int h) { return a.kv_div > 1 ? h / a.kv_div : h; };
   const int lp = a.log2_page;
   const int page_mask = (1 << lp) - 1;
   const int last_item = a.num_items - 1;
@@ -499,7 +502,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
     W.whi = min(u.te, W.base + win_steps * kStepTokens) - 1;
     W.wpage0 = u.tb >> lp;
     W.sp = sp;
-    W.head_off = (int64_t)u.kv_head * a.head_stride;
+    W.head_off = (int64_t)cache_head(u.kv_head) * a.head_stride;
     return W;
   };
 
@@ -1035,7 +1038,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
         W.whi = min(cu.te, base + w1 * kStepTokens) - 1;
         W.wpage0 = W.wlo >> lp;
         W.sp = s_pages[buf];
-        W.head_off = (int64_t)cu.kv_head * a.head_stride;
+        W.head_off = (int64_t)cache_head(cu.kv_head) * a.head_stride;
         const int s0 = w0 + ((wave - w0) % kWaves + kWaves) % kWaves;
         const int mine = s0 < w1 ? (w1 - s0 + kWaves - 1) / kWaves : 0;
         int m2 = max(4, (mine + 1) & ~1);

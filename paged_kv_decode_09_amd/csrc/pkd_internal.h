@@ -72,6 +72,9 @@ struct MergeRow {
 struct HostPlan {
   pkd_plan_params params{};
   pkd_plan_info info{};
+  // Blocks of query heads per kv head (kv_blocks(params)): the items count
+  // params.num_kv_heads * kv_blocks heads, and an item's kv_head is a block.
+  int32_t kv_blocks = 1;
   int32_t max_units = 0;   // most units of one request (per kv head)
   // items [0, steal_limit) have at least kStealMinBytes of K/V (the items
   // are sorted longest first): only these are published for stealing
@@ -92,6 +95,14 @@ void clear_error();
 // Validation of the parameters alone (no page table).
 pkd_status check_params(const pkd_plan_params& p);
 
+// Blocks of query heads per kv head. A unit carries at most kMaxGroup query
+// rows (G * Q, one MFMA tile); a group with more is split into the fewest
+// equal blocks of G / kv_blocks heads that fit, and each block is planned
+// and run as a kv head of its own: block b of kv head h is head
+// h * kv_blocks + b, its q heads (h * kv_blocks + b) * (G / kv_blocks) + ...,
+// and it reads kv head h's K/V (once per block). 1 when G * Q <= kMaxGroup.
+int32_t kv_blocks(const pkd_plan_params& p);
+
 // The planner: validates the page table, picks the chunk size, builds the
 // work units and spreads them over `num_slots` workgroups (the decode
 // workgroups that fit on the GPU at once). Pure host code.
@@ -110,7 +121,8 @@ pkd_status block_table_csr(const pkd_plan_params& p, const int32_t* seq_lens,
 
 // Capacities of a graph plan for p.batch_size requests holding at most
 // max_pages pages in all, on a launch of `slots` workgroups: the most units
-// per kv head the planner can make (all requests, and one request).
+// per item head (kv head and block of its q heads) the planner can make (all
+// requests, and one request).
 void graph_capacities(const pkd_plan_params& p, int32_t max_pages, int64_t slots,
                       int64_t* units_total, int64_t* units_one);
 
@@ -151,10 +163,11 @@ struct DecodeArgs {
   int32_t slot_stride;  // elements between tokens of a page
   int32_t head_stride;  // elements between kv heads of a page
   int32_t num_qo_heads;
-  int32_t num_kv_heads;
-  int32_t group;        // G
+  int32_t num_kv_heads; // heads of the items: kv heads times kv_div
+  int32_t kv_div;       // blocks of q heads per kv head: an item's kv_head / kv_div is the cache's
+  int32_t group;        // q heads per item head: G / kv_div
   int32_t q_len;        // Q, query tokens per request
-  int32_t cols;         // G * Q <= kMaxGroup: query rows of a unit
+  int32_t cols;         // group * Q <= kMaxGroup: query rows of a unit
   int32_t window_left;  // -1, or the left window of each query token
   int32_t alibi;        // nonzero: ALiBi bias on the logits
   // ROPE_LLAMA: [head_dim/2][2] rotary frequencies in revolutions per token

@@ -94,11 +94,6 @@ pkd_status check_params(const pkd_plan_params& p) {
     return fail(PKD_EINVAL,
                 fmt("num_qo_heads %d is not a multiple of num_kv_heads %d",
                     p.num_qo_heads, p.num_kv_heads));
-  const int32_t group = p.num_qo_heads / p.num_kv_heads;
-  if (group > kMaxGroup)
-    return fail(PKD_EUNSUPPORTED,
-                fmt("group size %d (num_qo_heads/num_kv_heads) exceeds %d",
-                    group, kMaxGroup));
   if (p.pos_encoding_mode == PKD_POS_ROPE_LLAMA) {
     if (!(p.rope_scale > 0.0f) || !std::isfinite(p.rope_scale) || !(p.rope_theta > 0.0f) ||
         !std::isfinite(p.rope_theta))
@@ -111,10 +106,10 @@ pkd_status check_params(const pkd_plan_params& p) {
                                 p.pos_encoding_mode));
   if (p.q_len_per_req < 0)
     return fail(PKD_EINVAL, fmt("q_len_per_req %d < 0", p.q_len_per_req));
-  if ((int64_t)group * q_len_of(p) > kMaxGroup)
+  if (q_len_of(p) > kMaxGroup)
     return fail(PKD_EUNSUPPORTED,
-                fmt("group size %d x q_len_per_req %d exceeds %d query rows per kv head",
-                    group, q_len_of(p), kMaxGroup));
+                fmt("q_len_per_req %d exceeds %d query rows per kv head", q_len_of(p),
+                    kMaxGroup));
   if (p.head_dim != 64 && p.head_dim != 128 && p.head_dim != 256)
     return fail(PKD_EUNSUPPORTED,
                 fmt("head_dim %d not in {64, 128, 256}", p.head_dim));
@@ -145,6 +140,13 @@ pkd_status check_params(const pkd_plan_params& p) {
     return fail(PKD_EINVAL,
                 "fixed_split_size and disable_split_kv are mutually exclusive");
   return PKD_OK;
+}
+
+int32_t kv_blocks(const pkd_plan_params& p) {
+  const int32_t G = p.num_qo_heads / p.num_kv_heads, Q = q_len_of(p);
+  for (int32_t nb = 1; nb < G; ++nb)
+    if (G % nb == 0 && (int64_t)(G / nb) * Q <= kMaxGroup) return nb;
+  return G;
 }
 
 int32_t decode_wgs_per_cu_table(const pkd_plan_params& p) {
@@ -195,6 +197,9 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
   pkd_status st = check_params(p);
   if (st != PKD_OK) return st;
   const int32_t B = p.batch_size;
+  // heads of the items: every kv head once per block of its query heads
+  const int32_t nb = kv_blocks(p);
+  const int32_t H = p.num_kv_heads * nb;
   if (B > 0 && (indptr == nullptr || last_page_len == nullptr))
     return fail(PKD_EINVAL, "indptr / last_page_len must not be NULL");
   if (num_slots < 1) return fail(PKD_EINVAL, fmt("num_slots %d < 1", num_slots));
@@ -256,12 +261,12 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
   } else if (B > 0) {
     // units of about a kUnitsPerWorkgroup-th of a workgroup's share, so
     // that no single long request decides when the last workgroup ends
-    const int64_t rows = (int64_t)(p.num_qo_heads / p.num_kv_heads) * q_len_of(p);
+    const int64_t rows = (int64_t)(p.num_qo_heads / H) * q_len_of(p);
     const int64_t units_wanted =
         std::max<int64_t>(1, slots * kUnitsPerWorkgroup * kSplitRowsRef /
                                  std::max<int64_t>(kSplitRowsRef, rows));
     {
-      const int64_t total = attended * p.num_kv_heads;
+      const int64_t total = attended * H;
       int64_t quantum = kUnitQuantum, unit;
       if (total <= slots * kUnitQuantum) {
         // A batch too small to give every workgroup a unit of the usual
@@ -295,6 +300,7 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
   };
   std::vector<Unit> units;
   out->params = p;
+  out->kv_blocks = nb;
   out->items.clear();
   out->merges.clear();
   out->max_units = 0;
@@ -355,7 +361,7 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
       out->merges.push_back(MergeRow{i, partials, (int32_t)n, 0});
     }
     for (int64_t c = 0; c < n; ++c) {
-      for (int32_t h = 0; h < p.num_kv_heads; ++h) {
+      for (int32_t h = 0; h < H; ++h) {
         Unit u;
         u.it.request = i;
         u.it.kv_head = h;
@@ -399,7 +405,7 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
   if (out->steal_limit <= (int64_t)units.size() - nwg) out->steal_limit = 0;
 
   // the merge counters are addressed with 32-bit byte offsets
-  if ((int64_t)B * p.num_kv_heads * (1 + (out->max_units + kMergeGroup - 1) / kMergeGroup) * 4 >
+  if ((int64_t)B * H * (1 + (out->max_units + kMergeGroup - 1) / kMergeGroup) * 4 >
       INT32_MAX / 2)
     return fail(PKD_EUNSUPPORTED, "too many split requests for the merge counters");
   // the merge addresses one request's partial states with 32-bit offsets
@@ -425,12 +431,12 @@ pkd_status build_host_plan(const pkd_plan_params& p, const int32_t* indptr,
 }
 
 // Capacities of a graph plan for B requests holding at most max_pages pages
-// in all: units per kv head (all requests, and one request) from the
+// in all: units per item head (all requests, and one request) from the
 // planner's rules (at most one unit per started chunk and sub-chunk under a
 // fixed split). Under its own split the units are of at least kUnitQuantum
 // tokens, beyond one per request, or, for a batch of at most
 // slots * kUnitQuantum tokens over all kv heads, chunks of at least half that
-// on the chunk grid: at most 2 * slots / num_kv_heads of them per kv head,
+// on the chunk grid: at most 2 * slots / item heads of them per item head,
 // beyond two per request.
 void graph_capacities(const pkd_plan_params& p, int32_t max_pages, int64_t slots,
                       int64_t* units_total, int64_t* units_one) {
@@ -448,7 +454,7 @@ void graph_capacities(const pkd_plan_params& p, int32_t max_pages, int64_t slots
     // (a small batch's units are chunks on the grid: a request's first one
     // may start inside a chunk, one more unit per request)
     const int64_t small = std::min<int64_t>(M * P / (kUnitQuantumTokens / 2),
-                                            2 * slots / std::max(1, p.num_kv_heads));
+                                            2 * slots / ((int64_t)p.num_kv_heads * kv_blocks(p)));
     const int64_t full = M * P / kUnitQuantumTokens;
     *units_total = std::max(full + B, small + 2 * B);
     *units_one = std::max(full + 1, small + 2);

@@ -18,7 +18,8 @@ namespace {
 
 int check(const pkd_plan_params& p, const std::vector<int32_t>& indptr,
           const std::vector<int32_t>& last, const pkd::HostPlan& h) {
-  const int B = p.batch_size, H = p.num_kv_heads, P = p.page_size;
+  // heads of the items: each kv head once per block of its query heads
+  const int B = p.batch_size, H = p.num_kv_heads * h.kv_blocks, P = p.page_size;
   const int Q = p.q_len_per_req > 1 ? p.q_len_per_req : 1;
   // expected[i][h]: next token the units must start at, per (request, head)
   std::vector<std::vector<int64_t>> next(B, std::vector<int64_t>(H, -1));
@@ -143,9 +144,14 @@ int main(int argc, char** argv) {
         int64_t tot = 0, one = 0, most = 0;
         pkd::graph_capacities(p, indptr[B], std::max(1, slots), &tot, &one);
         for (const auto& it : h.items) most = std::max<int64_t>(most, it.num_chunks);
-        if ((int64_t)h.items.size() > tot * p.num_kv_heads || most > one)
+        const int heads = p.num_kv_heads * h.kv_blocks;
+        if (h.kv_blocks != pkd::kv_blocks(p) ||
+            (int64_t)(p.num_qo_heads / heads) * (p.q_len_per_req > 1 ? p.q_len_per_req : 1) > 16 ||
+            p.num_qo_heads % heads != 0)
+          return fprintf(stderr, "kv_blocks %d (iteration %d)\n", h.kv_blocks, n), 1;
+        if ((int64_t)h.items.size() > tot * heads || most > one)
           return fprintf(stderr, "graph capacity %lld x %d heads / %lld below %zu items / %lld "
-                         "chunks (iteration %d)\n", (long long)tot, p.num_kv_heads,
+                         "chunks (iteration %d)\n", (long long)tot, heads,
                          (long long)one, h.items.size(), (long long)most, n), 1;
         ++plans;
         continue;

@@ -43,7 +43,6 @@ def query(indptr, last, num_cus=256, **kw):
 
 @pytest.mark.parametrize("kw,indptr,last,status,needle", [
     (dict(num_qo_heads=6, num_kv_heads=4), [0, 1], [1], pkd.PKD_EINVAL, "multiple"),
-    (dict(num_qo_heads=34, num_kv_heads=2), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "group size 17"),
     (dict(head_dim=96), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "head_dim 96"),
     (dict(page_size=12), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "page_size 12"),
     (dict(page_size=512), [0, 1], [1], pkd.PKD_EUNSUPPORTED, "page_size 512"),
@@ -61,7 +60,7 @@ def query(indptr, last, num_cus=256, **kw):
     (dict(q_len_per_req=-1), [0, 1], [1], pkd.PKD_EINVAL, "q_len_per_req -1"),
     (dict(pos_encoding_mode="ROPE_LLAMA", rope_theta=-1.0), [0, 1], [1], pkd.PKD_EINVAL, "must be positive"),
     (dict(pos_encoding_mode="XPOS"), [0, 1], [1], pkd.PKD_EINVAL, "pos_encoding_mode -1"),
-    (dict(q_len_per_req=5), [0, 1], [8], pkd.PKD_EUNSUPPORTED, "group size 4 x q_len_per_req 5"),
+    (dict(q_len_per_req=17), [0, 1], [17], pkd.PKD_EUNSUPPORTED, "q_len_per_req 17 exceeds 16"),
     (dict(q_len_per_req=3), [0, 1, 2], [9, 2], pkd.PKD_EINVAL, "request 1 has kv_len 2 < q_len_per_req 3"),
     (dict(sm_scale=float("inf")), [0, 1], [1], pkd.PKD_EINVAL, "sm_scale"),
 ])
@@ -271,6 +270,24 @@ def test_small_batch_units_of_one_step_per_wavefront():
     # a batch that fills the workgroups keeps units of at least 256 tokens
     info, items = query([0, 16 * 64], [16], num_qo_heads=64, num_kv_heads=64)
     assert info.split_pages * 16 >= 256
+
+
+@pytest.mark.parametrize("nq,nkv,Q,blocks", [
+    (32, 1, 1, 2), (64, 2, 1, 2), (48, 1, 1, 3), (34, 2, 1, 17), (8, 1, 4, 2), (16, 2, 3, 2),
+    (8, 2, 4, 1)])
+def test_large_groups_split_into_blocks_of_query_heads(nq, nkv, Q, blocks):
+    # G * Q query rows above 16 (one MFMA tile): each kv head's q heads go in
+    # the fewest equal blocks that fit, each planned as a head of its own
+    # (item kv_head = kv head * blocks + block), every block tiling the
+    # request as a kv head does
+    lens = np.array([300, 5000, 40])
+    pt = wl.page_table_for(lens, 16, "perm_used", np.random.default_rng(3))
+    info, items = query(pt.indptr, pt.last_page_len, num_qo_heads=nq, num_kv_heads=nkv,
+                        q_len_per_req=Q)
+    heads = nkv * blocks
+    assert (nq // heads) * Q <= 16 and nq % heads == 0
+    assert sorted({it.kv_head for it in items}) == list(range(heads))
+    coverage(items, heads, lens, [0] * len(lens))
 
 
 def test_empty_batch_plans_nothing():
