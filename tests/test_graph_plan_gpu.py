@@ -38,11 +38,13 @@ def tables(w, seeds):
     return out
 
 
-@pytest.mark.parametrize("split,Q,pos", [(None, 1, "NONE"), (2, 1, "NONE"), ("off", 1, "NONE"),
-                                         (None, 2, "NONE"), (None, 1, "ROPE_LLAMA"),
-                                         (2, 2, "ALIBI")])
-def test_graph_replays_follow_each_new_plan(split, Q, pos):
-    w = wl.small_workload(seed=79, batch=6, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+# (the last two: 32 and 20 q heads per kv head, run in blocks of q heads)
+@pytest.mark.parametrize("split,Q,pos,nq", [(None, 1, "NONE", 8), (2, 1, "NONE", 8),
+                                            ("off", 1, "NONE", 8), (None, 2, "NONE", 8),
+                                            (None, 1, "ROPE_LLAMA", 8), (2, 2, "ALIBI", 8),
+                                            (None, 1, "NONE", 64), (2, 2, "ALIBI", 40)])
+def test_graph_replays_follow_each_new_plan(split, Q, pos, nq):
+    w = wl.small_workload(seed=79, batch=6, num_qo_heads=nq, num_kv_heads=2, head_dim=128,
                           q_dtype="bf16", kv_dtype="bf16", o_dtype="bf16", layout="HND",
                           q_len_per_req=Q, pages="perm_pool", pool_pages=POOL)
     say(w, "split", split)
@@ -50,7 +52,7 @@ def test_graph_replays_follow_each_new_plan(split, Q, pos):
     kw = dict(q_data_type=torch.bfloat16, q_len_per_req=Q,
               fixed_split_size=split if isinstance(split, int) else None,
               disable_split_kv=split == "off", pos_encoding_mode=pos)
-    sinks = torch.linspace(-2.0, 3.0, 8, device="cuda") if pos != "NONE" else None
+    sinks = torch.linspace(-2.0, 3.0, nq, device="cuda") if pos != "NONE" else None
     dev = "cuda"
     wrapper = pkd.CUDAGraphBatchDecodeWithPagedKVCacheWrapper(
         torch.empty(64 << 20, dtype=torch.uint8, device=dev),
@@ -59,12 +61,12 @@ def test_graph_replays_follow_each_new_plan(split, Q, pos):
         torch.empty(w.batch, dtype=torch.int32, device=dev), kv_layout="HND")
     cases = tables(w, [1, 2, 3, 4])
     rows = w.batch * Q
-    q_static = torch.empty((rows, 8, 128), dtype=torch.bfloat16, device=dev)
-    o_static = torch.empty((rows, 8, 128), dtype=torch.bfloat16, device=dev)
-    l_static = torch.empty((rows, 8), dtype=torch.float32, device=dev)
+    q_static = torch.empty((rows, nq, 128), dtype=torch.bfloat16, device=dev)
+    o_static = torch.empty((rows, nq, 128), dtype=torch.bfloat16, device=dev)
+    l_static = torch.empty((rows, nq), dtype=torch.float32, device=dev)
     pt0, q0 = cases[0]
     wrapper.plan(pt0.indptr, torch.from_numpy(pt0.indices).to(dev), pt0.last_page_len,
-                 8, 2, 128, 16, **kw)
+                 nq, 2, 128, 16, **kw)
     q_static.copy_(q0)
     wrapper.run(q_static, pool, out=o_static, lse=l_static, sinks=sinks)   # warm-up, eager
     torch.cuda.synchronize()
@@ -75,14 +77,14 @@ def test_graph_replays_follow_each_new_plan(split, Q, pos):
     for k, (pt, q) in enumerate(cases + cases[:1]):
         say("page table", k, "pages", int(pt.indptr[-1]))
         wrapper.plan(pt.indptr, torch.from_numpy(pt.indices).to(dev), pt.last_page_len,
-                     8, 2, 128, 16, **kw)
+                     nq, 2, 128, 16, **kw)
         q_static.copy_(q)
         o_static.zero_()
         graph.replay()
         torch.cuda.synchronize()
         # an ordinary plan of the same page table, run eagerly
         idx = torch.from_numpy(pt.indices).to(dev)
-        plain = pkd.PagedDecodePlan(pt.indptr, idx, pt.last_page_len, 8, 2, 128, 16,
+        plain = pkd.PagedDecodePlan(pt.indptr, idx, pt.last_page_len, nq, 2, 128, 16,
                                     kv_layout="HND", **kw)
         o_ref, l_ref = plain.run(q, pool, return_lse=True, sinks=sinks)
         torch.cuda.synchronize()
