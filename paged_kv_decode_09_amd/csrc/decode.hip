@@ -22,12 +22,15 @@
 //    8 rows per load instruction) into registers, one step ahead, and go to
 //    the wave's LDS copies of the step.
 //  * q.K^T on MFMA 16x16x32: K rows, read back from LDS in the operand
-//    layout, are the A operand; the G*Q <= 16 query rows of the kv head are
-//    the B operand (columns past them repeat row 0 and are never written).
+//    layout, are the A operand; the item's G*Q <= 16 query rows are the B
+//    operand (columns past them repeat row 0 and are never written). A kv
+//    head with more query rows is planned as blocks of its q heads, each an
+//    item head of its own over the same K/V.
 //    Result lane l holds the logits of tokens 8*(l/16)+4*tile+i for row l%16.
 //  * P.V on MFMA as O^T = V^T P^T. P^T is what each lane holds after the
 //    softmax, so it needs no data movement; it enters as a hi + lo pair in
-//    the operand type (two MFMAs). V^T comes from the LDS copy of the step's
+//    the operand type (two MFMAs; hi alone in the RoPE instances, whose
+//    rounded operands already move p as much). V^T comes from the LDS copy of the step's
 //    V rows read with ds_read_b64_tr_b16 (16-bit V) or ds_read_b64_tr_b8
 //    (E4M3 V, converted after the read).
 //  * Online softmax in base 2 (v_exp_f32): one running max per head, made
@@ -258,7 +261,7 @@ struct Geo {
   // Steps of K/V rows held in registers: the next step's loads are issued
   // before the current step is computed.
   static constexpr int kStages = 2;
-  // LDS row pitch of the V copy; the pad staggers rows across banks.
+  // LDS row pitch of the K and V copies; the pad staggers rows across banks.
   static constexpr int kVPitch = kRowBytes + (KV8 ? 16 : 32);
   static constexpr int kVBytes = kStepTokens * kVPitch;
   // K rows are staged in a region of their own, after the V rows
@@ -307,7 +310,7 @@ __device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t r, uint32
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCoherentPolicy);
 }
 
-// merge_states for one (request, kv head) of a split request: fold the G
+// merge_states for one (request, item head) of a split request: fold the G
 // heads' states of `count` workspace slots first, first + stride, ...
 // (normalised outputs, base-2 LSE) by log-sum-exp, in slot order. The
 // result goes to o and the natural-log lse (out_slot < 0), or, as a state
