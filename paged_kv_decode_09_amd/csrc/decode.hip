@@ -591,6 +591,11 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
   // Tokens column n may see in the current unit: up to its query token's
   // position, and from its window start (set per unit).
   int col_lo = 0, col_hi = 0;
+  // Tokens every column sees (wave-uniform, set per unit): from the last
+  // query token's window start to the first query token's position.
+  int vis_lo = 0, vis_hi = -1;
+  // per-step work trimmed where it leaves the bits unchanged (see consume)
+  constexpr bool kTrimStep = ROPE && HD <= 128;
   // ALiBi slope of column n's q head, in the units the logits are in before
   // the cap (base 2 without a cap); 0 without ALiBi, which leaves every
   // logit's bits unchanged.
@@ -798,17 +803,37 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
     const int lo = max(W.wlo, col_lo), hi = min(W.whi, col_hi);
     float x[8];
     float mx = -INFINITY;
+    // A step wholly inside every column's visible range (all of them contain
+    // [max(wlo, vis_lo), min(whi, vis_hi)]) needs no mask, and without ALiBi
+    // no bias: the same bits, fewer instructions. Only the RoPE instances up
+    // to head_dim 128, whose steps are bound by instruction issue, take this
+    // path (serving_rope -1.7 us); elsewhere the second path costs more than
+    // it saves (gemma2_decode +5, fp8_kv +2 us).
+    if (kTrimStep && !a.alibi && t0 >= max(W.wlo, vis_lo) &&
+        t0 + kStepTokens - 1 <= min(W.whi, vis_hi)) {
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
+      for (int tile = 0; tile < 2; ++tile) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 8 * g + 4 * tile + i;
-        float v = sc[tile][i] * a.logit_scale;
-        v = __builtin_fmaf(col_slope, (float)(t - col_hi), v);   // ALiBi
-        if constexpr (CAP) v = a.cap * tanh_from_exp(v * a.inv_cap) * kLog2e;
-        v = (t >= lo && t <= hi) ? v : -INFINITY;
-        x[4 * tile + i] = v;
-        mx = fmaxf(mx, v);
+        for (int i = 0; i < 4; ++i) {
+          float v = sc[tile][i] * a.logit_scale;
+          if constexpr (CAP) v = a.cap * tanh_from_exp(v * a.inv_cap) * kLog2e;
+          x[4 * tile + i] = v;
+          mx = fmaxf(mx, v);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 8 * g + 4 * tile + i;
+          float v = sc[tile][i] * a.logit_scale;
+          v = __builtin_fmaf(col_slope, (float)(t - col_hi), v);   // ALiBi
+          if constexpr (CAP) v = a.cap * tanh_from_exp(v * a.inv_cap) * kLog2e;
+          v = (t >= lo && t <= hi) ? v : -INFINITY;
+          x[4 * tile + i] = v;
+          mx = fmaxf(mx, v);
+        }
       }
     }
     mx = wave_max_over_groups(mx);
@@ -841,6 +866,15 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
         pwl[i] = O::pack(x[2 * i] - (float)pop[2 * i], x[2 * i + 1] - (float)pop[2 * i + 1]);
     }
     const v8 pop_lo = __builtin_bit_cast(v8, pwl);
+    // the output sums to the new maximum: with kTrimStep here and only when
+    // some column's maximum moved (alpha 1 everywhere gives the same bits),
+    // else with each MFMA below
+    if constexpr (kTrimStep) {
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+        for (int b = 0; b < G_::kPvMfma; ++b) acc[b] *= alpha;
+      }
+    }
     // ---- O^T += V^T P^T, two MFMAs (hi, lo) per 16 hd columns
 #pragma unroll
     for (int b = 0; b < G_::kPvMfma; ++b) {
@@ -858,7 +892,9 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
         vop = __builtin_bit_cast(v8, (u32x4){l2[0], l2[1], h2[0], h2[1]});
       }
       f32x4 c = acc[b];
-      c[0] *= alpha; c[1] *= alpha; c[2] *= alpha; c[3] *= alpha;
+      if constexpr (!kTrimStep) {
+        c[0] *= alpha; c[1] *= alpha; c[2] *= alpha; c[3] *= alpha;
+      }
       if constexpr (kPLo) c = O::mfma(vop, pop_lo, c);
       acc[b] = O::mfma(vop, pop, c);
     }
@@ -1003,6 +1039,8 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
       q_turned = false;
       col_hi = cu.qpos + col_tok;
       col_lo = a.window_left < 0 ? 0 : col_hi - a.window_left;
+      vis_hi = cu.qpos;
+      vis_lo = a.window_left < 0 ? 0 : cu.qpos + a.q_len - 1 - a.window_left;
       if (a.alibi) {
         // the ALiBi paper's slopes over the q heads (n2: the power of two
         // at or below num_qo_heads; the heads past it take odd powers of
