@@ -20,6 +20,16 @@ namespace {
 // such launch on its stream. A launch on another stream first waits for that
 // event on the GPU, so launches that share the state never overlap, with no
 // host synchronisation. Launches recorded into a HIP graph are not tracked.
+// The event of a RunOrder is only ever waited on by another stream of the
+// same GPU (hipStreamWaitEvent), never synchronised with or queried from the
+// host. It is created without timing and without the system-scope fence that
+// hipEventRecord otherwise adds: what the later launch needs is the earlier
+// kernel's completion (its writes to the plan's state are device-scope
+// atomics and device-coherent stores). Recorded after every launch, the
+// fence cost each eager call about 1.7 us of GPU time (the class example's
+// batch: 15.2 against 13.6 us per call; no record at all: 12.4 us).
+constexpr unsigned kOrderEventFlags = hipEventDisableTiming | hipEventDisableSystemFence;
+
 struct RunOrder {
   std::mutex mu;
   hipEvent_t ev = nullptr;    // created before the first launch
@@ -199,7 +209,7 @@ pkd_status prepare_static_order(int dev) {
   if (dev < 0 || dev >= kMaxDevices) return PKD_OK;
   std::lock_guard<std::mutex> lock(g_static_order[dev].mu);
   if (g_static_order[dev].ev != nullptr) return PKD_OK;
-  const hipError_t e = hipEventCreateWithFlags(&g_static_order[dev].ev, hipEventDisableTiming);
+  const hipError_t e = hipEventCreateWithFlags(&g_static_order[dev].ev, kOrderEventFlags);
   if (e != hipSuccess) return hip_fail(e, "creating the static workspace's order event");
   return PKD_OK;
 }
@@ -325,7 +335,7 @@ pkd_status create_plan(const pkd_plan_params* params, const int32_t* indptr,
         pkd::workspace_lse_offset(p->cap_partials, Q * params->num_qo_heads, params->head_dim) +
         (size_t)p->cap_partials * Q * params->num_qo_heads * 4;
   }
-  e = hipEventCreateWithFlags(&p->order.ev, hipEventDisableTiming);
+  e = hipEventCreateWithFlags(&p->order.ev, kOrderEventFlags);
   if (e == hipSuccess) {
     const pkd_status so = prepare_static_order(dev);
     if (so != PKD_OK) {
