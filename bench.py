@@ -301,13 +301,25 @@ def main():
     for k in range(base):
         call(k)
     torch.cuda.synchronize()
+    def warm_eager():
+        """WARM_S seconds of back-to-back eager passes: the GPU's clocks drop
+        while it idles and take tens of milliseconds of work to come back."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < WARM_S:
+            for k in range(calls):
+                call(base + k)
+            torch.cuda.synchronize()
+
+    warm_eager()
     # Per-call protocol: HIP events around each single call, every call
     # preceded by an untimed 1 GiB fill that evicts the L2 and the Infinity
-    # Cache ("cold"), and the same without the fill on one pool ("hot").
-    # Taken before the graph so that the graph's replays stay the last
-    # launches of a run.
+    # Cache ("cold"), and the same without the fill on one pool ("hot"). The
+    # fills keep the GPU busy between calls, so the clocks stay up. Taken
+    # before the graph so that the graph's replays stay the last launches of
+    # a run.
     flushed = per_call_protocol(call, base, args.flush_calls, dev) if args.flush_calls > 0 else None
     # Eager pass: K steps launched from the host (the eager per-call figure).
+    warm_eager()
     t0 = time.perf_counter()
     for k in range(calls):
         call(base + k)
