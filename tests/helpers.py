@@ -180,6 +180,75 @@ def rope_lse_bounds(w, case, requests, theta, scale, base=LSE_TOL, sigmas=6.0):
     return out
 
 
+def rope_o_bounds(w, case, requests, theta, scale, ref_o, sigmas=6.0, base=True,
+                  parts=("operands", "p")):
+    """Elementwise o bound for ROPE_LLAMA runs, shaped like ref_o
+    [len(requests) * Q, nq, hd]: o_bounds (the tolerance, or the output's own
+    rounding) plus `sigmas` standard deviations of the error that the RoPE
+    instances' roundings add to o. Besides the rotated q and keys rounded to
+    the q dtype (the logit errors dx_t of rope_lse_bounds), these instances
+    take P into P.V as a single operand term: p rounded to the q dtype, with
+    relative error e_t. To first order
+        do_j = sum_t p_t (dx_t - sum_s p_s dx_s) v_tj + sum_t p_t e_t v_tj,
+    and with all rounding errors independent and zero-mean
+        var(do_j) = sm^2 [ sum_d var(dq_d) (sum_t p_t k'_td (v_tj - o_j))^2
+                           + sum_t p_t^2 (v_tj - o_j)^2 sum_d q'_d^2 var(dk_td) ]
+                    + sum_t var(p_t e_t) v_tj^2,
+    the last from rounding p_t / max_s p_s (the kernel rounds p against its
+    running maximum) scaled back. q', k', p, v and o are exact fp64 values;
+    the soft cap's derivative (at most 1) is left out, which only widens the
+    bound. base=False returns the sigmas-standard-deviation term alone;
+    `parts` selects the error sources ("operands": q and keys, "p": P)."""
+    import oracle as orc
+    Q = w.q_len_per_req
+    reqs = list(requests)
+    pool, indptr, indices, last = sub_pool(case, reqs)
+    rows = torch.tensor(rows_of(w, reqs))
+    qn = orc.widen(wl.raw_numpy(case.q[rows], w.q_dtype), w.q_dtype)
+    pn = wl.raw_numpy(pool, w.kv_dtype)
+    lens = orc.kv_lengths(indptr, last, w.page_size)
+    nq, nkv, hd = w.num_qo_heads, w.num_kv_heads, w.head_dim
+    G = nq // nkv
+    sm = w.sm_scale
+    out = np.array(o_bounds(w, ref_o), dtype=np.float64) if base else \
+        np.zeros(np.shape(ref_o))
+    for r in range(len(reqs)):
+        L = int(lens[r])
+        K, V = orc.gather_request(pn[:, 0], pn[:, 1], w.layout, indices, indptr, r, L,
+                                  w.page_size)
+        Kf = orc.widen(K, w.kv_dtype, w.k_scale)                 # [L, nkv, hd]
+        Vf = orc.widen(V, w.kv_dtype, w.v_scale)
+        for j in range(Q):
+            pos = L - Q + j
+            s0 = 0 if w.window_left < 0 else max(0, pos - w.window_left)
+            Kr = orc.rope_rotate(Kf[s0:pos + 1].transpose(1, 0, 2),
+                                 np.arange(s0, pos + 1), theta, scale)  # [nkv, n, hd]
+            vk = _rne_error_var(Kr / w.k_scale, w.q_dtype) * w.k_scale ** 2
+            qr = orc.rope_rotate(qn[r * Q + j][:, None, :], [pos], theta, scale)[:, 0, :]
+            vq = _rne_error_var(qr, w.q_dtype)
+            for hq in range(nq):
+                h = hq // G
+                Vh = Vf[s0:pos + 1, h]                            # [n, hd]
+                x = sm * (Kr[h] @ qr[hq])
+                if w.logits_soft_cap > 0:
+                    x = w.logits_soft_cap * np.tanh(x / w.logits_soft_cap)
+                p = np.exp(x - x.max())
+                p /= p.sum()
+                D = Vh - p @ Vh                                   # v_tj - o_j
+                A = Kr[h].T @ (p[:, None] * D)                    # [d, j]
+                t1 = vq[hq] @ (A * A)
+                s = vk[h] @ (qr[hq] * qr[hq])                     # [n]
+                t2 = ((p * p * s)[:, None] * D * D).sum(0)
+                pm = p.max()
+                # (the maximum, p / pm = 1, is exact in any format: no error)
+                vp = np.where(p == pm, 0.0, _rne_error_var(p / pm, w.q_dtype) * pm * pm)
+                t3 = (vp[:, None] * Vh * Vh).sum(0)
+                var = (sm * sm * (t1 + t2) if "operands" in parts else 0.0) + \
+                    (t3 if "p" in parts else 0.0)
+                out[r * Q + j, hq] += sigmas * np.sqrt(var)
+    return out
+
+
 def o_bounds(w, ref):
     """Elementwise bound on |o - ref| for an output of dtype w.o_dtype: the
     max-abs tolerance, or, where the exact value is too large in magnitude
