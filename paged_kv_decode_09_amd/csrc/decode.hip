@@ -920,8 +920,13 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
   // return by the unit's end, late enough that near the end of the queue
   // the last units go to the workgroups about to need them.
   // Its first two units are items blockIdx.x and blockIdx.x + gridDim.x
-  // (the grid never exceeds the item count); later ones are tickets from
-  // the plan's counter, offset by twice the grid size.
+  // (a graph plan's grid may exceed the item count); later ones are tickets
+  // from the plan's counter, offset by twice the grid size. A workgroup
+  // takes tickets while it holds a unit nxt, so each workgroup whose second
+  // unit exists takes the valid tickets it gets and then exactly one past
+  // the end: a launch takes max(0, N - 2 grid) + max(0, min(grid, N - grid))
+  // tickets (N items), and the workgroup that takes the last one resets the
+  // counter for the next launch.
   //
   // A long enough held unit nxt (an item below a.steal_limit) is published
   // in a reserve slot from the time its ticket is known until cur's last
@@ -1063,12 +1068,12 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
       // Steps are processed in windows whose pages fit the LDS page table. A
       // wave takes every kWaves-th step of a window, one step ahead of the
       // loads (buffers A and B alternate); the count is padded to an even
-      // number >= 4 with steps past the window, which read clamped rows and
+      // number >= 2 with steps past the window, which read clamped rows and
       // whose tokens are all masked (no effect on the state). The first and
-      // the last half-step are peeled and the loop body runs at least once,
-      // so that the same loads are in flight on every path through it and the
-      // compiler's wait before a step covers that step's loads only. The last
-      // issue of the last window is the next unit's first step.
+      // the last step are peeled, and each pass of the loop between them
+      // issues and consumes two steps, so that the compiler's wait before a
+      // step covers that step's loads only. The last issue of the last
+      // window is the next unit's first step when there is a next unit.
       bool drop = false;      // cur was taken by another workgroup: no outputs
       int w0 = 0;
       do {
@@ -1082,7 +1087,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
         W.head_off = (int64_t)cache_head(cu.kv_head) * a.head_stride;
         const int s0 = w0 + ((wave - w0) % kWaves + kWaves) % kWaves;
         const int mine = s0 < w1 ? (w1 - s0 + kWaves - 1) / kWaves : 0;
-        int m2 = max(4, (mine + 1) & ~1);
+        int m2 = max(2, (mine + 1) & ~1);
         if (w0 > 0) {
           // a later window: its pages replace the previous window's
           lds_barrier();
@@ -1110,13 +1115,15 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
           drop = __builtin_amdgcn_readfirstlane(s_drop) != 0;
           if (drop) {
             W.whi = W.wlo;
-            m2 = 4;
+            m2 = 2;
             w1 = nsteps;
           }
         }
         __builtin_amdgcn_sched_barrier(0);
         int j = 1;
-        do {
+        // (a guarded do-while: as a plain while loop the compiler keeps more
+        // registers live across it)
+        if (m2 > 2) do {
           issue(W, s0 + (j + 1) * kWaves, A);
           {
             // the ticket: in range for thread 0 in the last pass of the last
@@ -1135,9 +1142,9 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
           j += 2;
         } while (j + 1 < m2);
         {
-          // last issue: the next unit's first step after the last window,
-          // else a clamped surplus step of this window
-          const bool hand = w1 == nsteps;
+          // last issue: the next unit's first step after the last window if
+          // there is a next unit, else a clamped padding step of this window
+          const bool hand = w1 == nsteps && nxt < a.num_items;
           // Thread 0 claims nxt if it was published (after the last window);
           // the other lanes, and earlier windows, fall outside the buffer and
           // do nothing. The result is read with nxt's first step.
@@ -1146,6 +1153,13 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
                                     : 0x80000000u;
           claim = (unsigned)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32((int)kClaimStep, res_rsrc,
                                                                            coff, 0, 0);
+          {
+            // the ticket of a last window of two steps, whose loop above has
+            // no pass (out of range, and so nothing, in every other case)
+            const uint32_t toff = m2 == 2 && hand && threadIdx.x == 0 ? 0u : 0x80000000u;
+            const unsigned t2 = (unsigned)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, cnt_rsrc, toff, 0, 0);
+            tk = m2 == 2 ? t2 : tk;
+          }
           int cc[kRowBlocks], pp[kRowBlocks];
 #pragma unroll
           for (int b = 0; b < kRowBlocks; ++b) {
@@ -1166,7 +1180,16 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
       if ((int)threadIdx.x < nwpages) s_pages[buf ^ 1][threadIdx.x] = pgn;
       for (int i = threadIdx.x + kWaves * 64; i < nwpages; i += kWaves * 64)
         s_pages[buf ^ 1][i] = npidx[Wn.wpage0 + i];
-      if (threadIdx.x == 0) s_ticket[par] = nxt < a.num_items ? 2 * (int)gridDim.x + (int)tk : a.num_items;
+      if (threadIdx.x == 0) {
+        s_ticket[par] = nxt < a.num_items ? 2 * (int)gridDim.x + (int)tk : a.num_items;
+        // the last ticket of the launch: every ticket has been taken, so the
+        // counter can be reset for the next launch
+        const int grid = (int)gridDim.x;
+        const int last_ticket =
+            max(0, a.num_items - 2 * grid) + max(0, min(grid, a.num_items - grid)) - 1;
+        if (nxt < a.num_items && (int)tk == last_ticket)
+          __hip_atomic_store(a.counters, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       d_run = wave_sum_over_groups(d_run);
       float* sacc = reinterpret_cast<float*>(vl);   // [16 rows][HD], own region
       if (n < cols) {
@@ -1287,12 +1310,6 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
     if (cur < 0) break;
     nxt = a.num_items;
     claimed = false;
-  }
-  // The last workgroup out resets the counters for the next launch: every
-  // other workgroup has already taken its final ticket by then.
-  if (threadIdx.x == 0 && atomicAdd(&a.counters[1], 1) == (int)gridDim.x - 1) {
-    atomicExch(&a.counters[0], 0);
-    atomicExch(&a.counters[1], 0);
   }
 }
 

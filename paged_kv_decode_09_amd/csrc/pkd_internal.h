@@ -136,8 +136,9 @@ size_t workspace_lse_offset(int32_t num_partials, int32_t num_qo_heads,
 // ----------------------------------------------------------------- kernels
 
 struct DecodeArgs {
-  // counters[0]: next item to take; counters[1]: workgroups finished. Both
-  // are zero when a launch starts; the last workgroup to finish resets them.
+  // counters[0]: tickets taken (items beyond each workgroup's first two).
+  // Zero when a launch starts; the workgroup that takes the launch's last
+  // ticket resets it.
   int32_t* counters;
   // [2 * gridDim.x] reserve slots, two per workgroup (by unit parity): the
   // unit a workgroup holds beyond its current one, for workgroups whose own
