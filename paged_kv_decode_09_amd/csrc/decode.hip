@@ -439,8 +439,8 @@ struct Win {
   int64_t head_off;
 };
 
-template <int HD, bool QBF16, bool KV8, bool CAP, bool ROPE>
-__global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) void decode_kernel(DecodeArgs args) {
+template <int HD, bool QBF16, bool KV8, bool CAP, bool ROPE, bool SINGLE>
+__global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE, SINGLE)) void decode_kernel(DecodeArgs args) {
   DecodeArgs a = args;
   if (args.plan_header != nullptr) {
     // a graph plan: the launch was recorded once; the current page table's
@@ -451,9 +451,19 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
   }
   using G_ = Geo<HD, KV8>;
   using O = Op<QBF16>;
+  // SINGLE: one register buffer of K/V rows per wavefront, whose next loads
+  // leave as soon as a step is staged in LDS (decode_single tells which
+  // plans run such an instance). At head_dim 128 two workgroups share a
+  // compute unit, which keeps the loads in flight per SIMD of two buffers
+  // at one workgroup, and the rotation of one wavefront's keys fills the
+  // stalls of the other's.
+  constexpr bool kSingle = SINGLE;
+  static_assert(!SINGLE || (ROPE && (HD == 128 || (HD == 256 && !KV8))), "no such instance");
+  // (two workgroups' LDS must fit a compute unit at head_dim 128)
+  constexpr int kPageWinOf = kSingle && HD == 128 ? kPageWin / 2 : kPageWin;
   using v8 = typename O::v8;
   __shared__ __attribute__((aligned(16))) char smem[kWaves * G_::kWaveLds];
-  __shared__ int s_pages[2][kPageWin];   // first window of this unit / of the next
+  __shared__ int s_pages[2][kPageWinOf]; // first window of this unit / of the next
   __shared__ float s_m[kWaves][kMaxGroup];
   __shared__ float s_d[kWaves][kMaxGroup];
   __shared__ int s_ticket[2];
@@ -488,7 +498,7 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
   const int page_mask = (1 << lp) - 1;
   const int last_item = a.num_items - 1;
   // steps per window of pages held in LDS
-  const int win_steps = max(1, ((kPageWin - 1) << lp) >> 5);
+  const int win_steps = max(1, ((kPageWinOf - 1) << lp) >> 5);
   // Token (within a step) whose K row lane n loads for tiles 0 and 1: tile
   // rows 4g'+i then map to tokens 8g'+4*tile+i.
   const int tau0 = 8 * (n >> 2) + (n & 3);
@@ -654,14 +664,12 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
 
   // Attend step s of window W whose K/V rows are in st. A step wholly past
   // the window (the padding step of an odd count) changes nothing.
-  auto consume = [&](const Win& W, int s, const StepRegs<kNP>& st) {
+  // ---- the step's K and V rows to this wave's LDS copies (row = token
+  // within the step) as loaded. A wave's LDS accesses run in order, so the
+  // previous step's reads are done before these writes land.
+  auto stage = [&](const Win& W, int s, const StepRegs<kNP>& st) {
     const int t0 = W.base + s * kStepTokens;
     if (t0 > W.whi) return;
-    // ---- the step's K and V rows to this wave's LDS copies (row = token
-    // within the step) as loaded; K read back in the MFMA layout (lane
-    // (n, g) of tile t: 64-byte piece p of row tau_t from byte 16 g). A
-    // wave's LDS accesses run in order, so the previous step's reads are
-    // done before these writes land.
     char* kl = vl + G_::kVBytes;
 #pragma unroll
     for (int q = 0; q < kChunkBlocks; ++q)
@@ -672,6 +680,13 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
         *reinterpret_cast<u32x4*>(kl + off) = st.k[i / kNP][i % kNP];
         *reinterpret_cast<u32x4*>(vl + off) = st.v[i / kNP][i % kNP];
       }
+  };
+  // ---- attend the step staged in LDS: K read back in the MFMA layout (lane
+  // (n, g) of tile t: 64-byte piece p of row tau_t from byte 16 g)
+  auto attend = [&](const Win& W, int s) {
+    const int t0 = W.base + s * kStepTokens;
+    if (t0 > W.whi) return;
+    char* kl = vl + G_::kVBytes;
     // (With the rotary embedding at head_dim 256 and 16-bit K the pieces are
     // read pair by pair inside the rotation below: all sixteen at once would
     // not leave the registers the rotation needs.)
@@ -899,6 +914,10 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
       acc[b] = O::mfma(vop, pop, c);
     }
   };
+  auto consume = [&](const Win& W, int s, const StepRegs<kNP>& st) {
+    stage(W, s, st);
+    attend(W, s);
+  };
 
   // the partial outputs, for 16-byte device-coherent stores
   const __amdgpu_buffer_rsrc_t ws_o_rsrc =
@@ -1096,6 +1115,55 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE)) 
           for (int i = threadIdx.x; i < wpages; i += kWaves * 64) s_pages[buf][i] = pidx[W.wpage0 + i];
           lds_barrier();
           issue(W, s0, A);
+        }
+        if constexpr (kSingle) {
+          // one buffer: step s is staged, the next step's loads leave, then
+          // s is attended; a wave with no step here runs one padding step
+          int n1 = max(1, mine);
+          for (int k = 0; k < n1; ++k) {
+            const int s = s0 + k * kWaves;
+            stage(W, s, A);
+            __builtin_amdgcn_sched_barrier(0);
+            if (k == 0) {
+              load_next();
+              if (w0 == 0 && claimed) {
+                if (threadIdx.x == 0) s_drop = (claim & kStolen) != 0;
+                lds_barrier();
+                drop = __builtin_amdgcn_readfirstlane(s_drop) != 0;
+                if (drop) {
+                  W.whi = W.wlo;
+                  n1 = 1;
+                  w1 = nsteps;
+                }
+              }
+            }
+            if (k + 1 < n1) {
+              issue(W, s + kWaves, A);
+            } else {
+              const bool hand = w1 == nsteps && nxt < a.num_items;
+              const uint32_t coff = hand && nxt < a.steal_limit && threadIdx.x == 0
+                                        ? (uint32_t)(2 * blockIdx.x + (par ^ 1)) * 4u
+                                        : 0x80000000u;
+              claim = (unsigned)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32((int)kClaimStep, res_rsrc,
+                                                                               coff, 0, 0);
+              const uint32_t toff = hand && threadIdx.x == 0 ? 0u : 0x80000000u;
+              tk = (unsigned)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, cnt_rsrc, toff, 0, 0);
+              int cc[kRowBlocks], pp[kRowBlocks];
+#pragma unroll
+              for (int b = 0; b < kRowBlocks; ++b) {
+                const int cw = token(W, s + kWaves, lrow + kRowsPer * b);
+                const int pw = W.sp[(cw >> lp) - W.wpage0];
+                cc[b] = hand ? token(Wn, wave, lrow + kRowsPer * b) : cw;
+                pp[b] = hand ? hpg[b] : pw;
+              }
+              issue_rows(hand ? Wn : W, cc, pp, A);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            attend(W, s);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          w0 = w1;
+          continue;
         }
         // The scheduling barriers keep each issue ahead of the step it overlaps:
         // the loads must leave before the wait for the previous step's rows.
@@ -1382,15 +1450,24 @@ __global__ __launch_bounds__(kMergeRowsPerBlock * 64) void merge_kernel(MergeArg
     a.s_out[row] = M == -INFINITY ? -INFINITY : (M + __builtin_amdgcn_logf(den)) * kLn2;
 }
 
-// The kernel instance for (head_dim, q type, KV type, soft cap, RoPE).
+// The kernel instance for (head_dim, q type, KV type, soft cap, RoPE, one
+// K/V buffer).
 using DecodeFn = void (*)(DecodeArgs);
 
 template <bool QBF16, bool KV8, bool CAP, bool ROPE>
-DecodeFn pick_hd(int hd) {
+DecodeFn pick_hd(int hd, bool single) {
   switch (hd) {
-    case 64: return decode_kernel<64, QBF16, KV8, CAP, ROPE>;
-    case 128: return decode_kernel<128, QBF16, KV8, CAP, ROPE>;
-    default: return decode_kernel<256, QBF16, KV8, CAP, ROPE>;
+    case 64: return decode_kernel<64, QBF16, KV8, CAP, ROPE, false>;
+    case 128:
+      if constexpr (ROPE) {
+        if (single) return decode_kernel<128, QBF16, KV8, CAP, true, true>;
+      }
+      return decode_kernel<128, QBF16, KV8, CAP, ROPE, false>;
+    default:
+      if constexpr (ROPE && !KV8) {
+        if (single) return decode_kernel<256, QBF16, KV8, CAP, true, true>;
+      }
+      return decode_kernel<256, QBF16, KV8, CAP, ROPE, false>;
   }
 }
 
@@ -1399,12 +1476,14 @@ DecodeFn pick_types(const pkd_plan_params& p) {
   const bool cap = p.logits_soft_cap > 0.0f;
   const bool qbf = p.q_dtype == PKD_BF16;
   const bool kv8 = p.kv_dtype == PKD_E4M3;
+  const bool one = decode_single(p);
+  const int hd = p.head_dim;
   if (qbf) {
-    if (kv8) return cap ? pick_hd<true, true, true, ROPE>(p.head_dim) : pick_hd<true, true, false, ROPE>(p.head_dim);
-    return cap ? pick_hd<true, false, true, ROPE>(p.head_dim) : pick_hd<true, false, false, ROPE>(p.head_dim);
+    if (kv8) return cap ? pick_hd<true, true, true, ROPE>(hd, one) : pick_hd<true, true, false, ROPE>(hd, one);
+    return cap ? pick_hd<true, false, true, ROPE>(hd, one) : pick_hd<true, false, false, ROPE>(hd, one);
   }
-  if (kv8) return cap ? pick_hd<false, true, true, ROPE>(p.head_dim) : pick_hd<false, true, false, ROPE>(p.head_dim);
-  return cap ? pick_hd<false, false, true, ROPE>(p.head_dim) : pick_hd<false, false, false, ROPE>(p.head_dim);
+  if (kv8) return cap ? pick_hd<false, true, true, ROPE>(hd, one) : pick_hd<false, true, false, ROPE>(hd, one);
+  return cap ? pick_hd<false, false, true, ROPE>(hd, one) : pick_hd<false, false, false, ROPE>(hd, one);
 }
 
 DecodeFn pick_kernel(const pkd_plan_params& p) {

@@ -54,8 +54,27 @@ constexpr int64_t kStealMinBytes = 512 << 10;
 // them every dependent load at a unit boundary. Head_dim 64 (a quarter of
 // the bytes per step) uses three, or two with 16-bit K/V and the rotary
 // embedding, whose rotation needs more registers than a third of the file.
-constexpr int decode_waves_per_simd(int head_dim, bool kv8, bool rope) {
-  return head_dim >= 128 ? 1 : (rope && !kv8 ? 2 : 3);
+// An instance with one step of K/V rows in registers (`single`) runs two
+// workgroups per compute unit at head_dim 128.
+constexpr int decode_waves_per_simd(int head_dim, bool kv8, bool rope, bool single = false) {
+  return head_dim >= 128 ? (single && head_dim == 128 ? 2 : 1) : (rope && !kv8 ? 2 : 3);
+}
+
+// Plans whose kernel holds one step of K/V rows in registers per wavefront
+// instead of two (its next loads leave as soon as a step is staged in LDS):
+// RoPE at head_dim 128, or at 256 with 16-bit K/V, under the planner's own
+// split. The rotation keeps such a kernel busy issuing: at head_dim 128 a
+// second workgroup per compute unit fills the stalls of the first (the
+// serving batch with RoPE 119.5 -> 115.5 us, E4M3 KV with RoPE 550 -> 498),
+// at 256 the freed registers end its spills (Gemma-2-style with RoPE 772 ->
+// 751). Under a fixed split or with one unit per request the units can be
+// long, and a workgroup alone on its compute unit at the end streams at half
+// rate with one buffer (long context with RoPE 233 -> 268): those plans keep
+// two buffers.
+inline bool decode_single(const pkd_plan_params& p) {
+  return p.pos_encoding_mode == PKD_POS_ROPE_LLAMA && p.fixed_split_size <= 0 &&
+         !p.disable_split_kv &&
+         (p.head_dim == 128 || (p.head_dim == 256 && p.kv_dtype != PKD_E4M3));
 }
 
 // One split request: its workspace slots are partial_base ..

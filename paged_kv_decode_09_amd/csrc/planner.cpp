@@ -151,7 +151,7 @@ int32_t kv_blocks(const pkd_plan_params& p) {
 
 int32_t decode_wgs_per_cu_table(const pkd_plan_params& p) {
   return decode_waves_per_simd(p.head_dim, p.kv_dtype == PKD_E4M3,
-                               p.pos_encoding_mode == PKD_POS_ROPE_LLAMA);
+                               p.pos_encoding_mode == PKD_POS_ROPE_LLAMA, decode_single(p));
 }
 
 size_t workspace_lse_offset(int32_t num_partials, int32_t num_qo_heads,

@@ -166,17 +166,18 @@ def rope_lse_bounds(w, case, requests, theta, scale, base=LSE_TOL, sigmas=6.0):
             vk = _rne_error_var(Kr / w.k_scale, w.q_dtype) * w.k_scale ** 2
             qr = orc.rope_rotate(qn[r * Q + j][:, None, :], [pos], theta, scale)[:, 0, :]
             vq = _rne_error_var(qr, w.q_dtype)
-            for hq in range(nq):
-                h = hq // G
-                x = sm * (Kr[h] @ qr[hq])
+            for h in range(nkv):
+                # the G q heads of kv head h at once: columns of [n, G]
+                hs = slice(h * G, (h + 1) * G)
+                x = sm * (Kr[h] @ qr[hs].T)
                 if w.logits_soft_cap > 0:
                     x = w.logits_soft_cap * np.tanh(x / w.logits_soft_cap)
-                p = np.exp(x - x.max())
-                p /= p.sum()
-                kbar = p @ Kr[h]                                  # [hd]
-                var = sm * sm * (np.sum(vq[hq] * kbar * kbar) +
-                                 np.sum(p * p * (vk[h] @ (qr[hq] * qr[hq]))))
-                out[r * Q + j, hq] = base + sigmas * np.sqrt(var)
+                p = np.exp(x - x.max(axis=0))
+                p /= p.sum(axis=0)
+                kbar = p.T @ Kr[h]                                # [G, hd]
+                var = sm * sm * (np.sum(vq[hs] * kbar * kbar, axis=1) +
+                                 np.sum(p * p * (vk[h] @ (qr[hs] * qr[hs]).T), axis=0))
+                out[r * Q + j, hs] = base + sigmas * np.sqrt(var)
     return out
 
 
@@ -226,26 +227,35 @@ def rope_o_bounds(w, case, requests, theta, scale, ref_o, sigmas=6.0, base=True,
             vk = _rne_error_var(Kr / w.k_scale, w.q_dtype) * w.k_scale ** 2
             qr = orc.rope_rotate(qn[r * Q + j][:, None, :], [pos], theta, scale)[:, 0, :]
             vq = _rne_error_var(qr, w.q_dtype)
-            for hq in range(nq):
-                h = hq // G
+            for h in range(nkv):
+                # the G q heads of kv head h at once (columns of [n, G]); the
+                # sums over tokens t of terms in (v_tj - o_j) are expanded in
+                # powers of o_j, so that each is a product with V or V*V
+                hs = slice(h * G, (h + 1) * G)
                 Vh = Vf[s0:pos + 1, h]                            # [n, hd]
-                x = sm * (Kr[h] @ qr[hq])
+                V2 = Vh * Vh
+                x = sm * (Kr[h] @ qr[hs].T)                       # [n, G]
                 if w.logits_soft_cap > 0:
                     x = w.logits_soft_cap * np.tanh(x / w.logits_soft_cap)
-                p = np.exp(x - x.max())
-                p /= p.sum()
-                D = Vh - p @ Vh                                   # v_tj - o_j
-                A = Kr[h].T @ (p[:, None] * D)                    # [d, j]
-                t1 = vq[hq] @ (A * A)
-                s = vk[h] @ (qr[hq] * qr[hq])                     # [n]
-                t2 = ((p * p * s)[:, None] * D * D).sum(0)
-                pm = p.max()
-                # (the maximum, p / pm = 1, is exact in any format: no error)
-                vp = np.where(p == pm, 0.0, _rne_error_var(p / pm, w.q_dtype) * pm * pm)
-                t3 = (vp[:, None] * Vh * Vh).sum(0)
-                var = (sm * sm * (t1 + t2) if "operands" in parts else 0.0) + \
-                    (t3 if "p" in parts else 0.0)
-                out[r * Q + j, hq] += sigmas * np.sqrt(var)
+                p = np.exp(x - x.max(axis=0))
+                p /= p.sum(axis=0)
+                o = p.T @ Vh                                      # [G, hd]
+                kp = Kr[h].T @ p                                  # [d, G]: sum_t p_t k'_td
+                for g in range(G):
+                    # A_dj = sum_t p_t k'_td (v_tj - o_j)
+                    A = (Kr[h] * p[:, g:g + 1]).T @ Vh - np.outer(kp[:, g], o[g])
+                    t1 = vq[h * G + g] @ (A * A)
+                    s = vk[h] @ (qr[h * G + g] * qr[h * G + g])   # [n]
+                    wt = p[:, g] * p[:, g] * s
+                    t2 = wt @ V2 - 2.0 * o[g] * (wt @ Vh) + o[g] * o[g] * wt.sum()
+                    pg = p[:, g]
+                    pm = pg.max()
+                    # (the maximum, p / pm = 1, is exact in any format: no error)
+                    vp = np.where(pg == pm, 0.0, _rne_error_var(pg / pm, w.q_dtype) * pm * pm)
+                    t3 = vp @ V2
+                    var = (sm * sm * (t1 + t2) if "operands" in parts else 0.0) + \
+                        (t3 if "p" in parts else 0.0)
+                    out[r * Q + j, h * G + g] += sigmas * np.sqrt(np.maximum(var, 0.0))
     return out
 
 

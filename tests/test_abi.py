@@ -255,6 +255,25 @@ def test_auto_split_respects_minimum_unit():
     assert all(i.token_end - i.token_begin <= info.split_pages * 16 for i in items)
 
 
+@pytest.mark.parametrize("kw,per_cu", [
+    (dict(head_dim=128, pos_encoding_mode="ROPE_LLAMA"), 2),
+    (dict(head_dim=128, pos_encoding_mode="ROPE_LLAMA", kv_data_type="e4m3"), 2),
+    (dict(head_dim=256, pos_encoding_mode="ROPE_LLAMA"), 1),
+    (dict(head_dim=128, pos_encoding_mode="ROPE_LLAMA", fixed_split_size=16), 1),
+    (dict(head_dim=128, pos_encoding_mode="ROPE_LLAMA", disable_split_kv=True), 1),
+    (dict(head_dim=64, pos_encoding_mode="ROPE_LLAMA"), 2),
+    (dict(head_dim=128), 1),
+    (dict(head_dim=128, pos_encoding_mode="ALIBI"), 1),
+])
+def test_workgroups_per_compute_unit(kw, per_cu):
+    # RoPE at head_dim 128 under the planner's own split runs the kernel with
+    # one K/V buffer, two workgroups per compute unit; a fixed split or one
+    # unit per request keeps one workgroup (and two buffers)
+    info, _ = query([0, 200, 500], [16, 16], **kw)
+    assert info.workgroups_per_cu == per_cu
+    assert info.num_workgroups <= 256 * per_cu
+
+
 def test_small_batch_units_of_one_step_per_wavefront():
     # the class example's batch (64/8 heads, 1982 tokens): too small to give
     # each of 256 workgroups a unit of 256 tokens, so the units are of at most
