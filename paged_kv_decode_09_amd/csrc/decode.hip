@@ -13,14 +13,17 @@
 //
 // Design (MI355X-first, not the page's):
 //  * A persistent grid of workgroups of 4 wavefronts, one per compute unit
-//    (three at head_dim 64), that pipeline work items taken from a counter.
+//    (three at head_dim 64, two for the one-buffer RoPE instances at 128),
+//    that pipeline work items taken from a counter.
 //    Wavefront w takes the 32-token steps w, w+4, ... of an item; the four
 //    partial states are merged in LDS in wavefront order at the end, so the
 //    result depends only on the item's token range (bitwise batch invariance
 //    under a fixed split).
 //  * K and V rows arrive as whole 128-byte lines (non-temporal 16-byte loads,
 //    8 rows per load instruction) into registers, one step ahead, and go to
-//    the wave's LDS copies of the step.
+//    the wave's LDS copies of the step. The RoPE instances under the
+//    planner's own split hold one step in registers (SINGLE): its rows go to
+//    LDS and the next step's loads leave before the step is attended.
 //  * q.K^T on MFMA 16x16x32: K rows, read back from LDS in the operand
 //    layout, are the A operand; the item's G*Q <= 16 query rows are the B
 //    operand (columns past them repeat row 0 and are never written). A kv
