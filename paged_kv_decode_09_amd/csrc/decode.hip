@@ -144,6 +144,18 @@ __device__ __forceinline__ typename Op<BF16>::v8 e4m3x8(unsigned lo, unsigned hi
   return __builtin_bit_cast(typename Op<BF16>::v8, r);
 }
 
+// Eight E4M3 codes (words 0 and 1 of a piece, or 2 and 3 if `upper`) as
+// fp32, in order, two per scaled conversion (scale 1: exact).
+__device__ __forceinline__ void e4m3_f32x8(const u32x4& w, bool upper, float (&x)[8]) {
+  const unsigned lo = upper ? w[2] : w[0], hi = upper ? w[3] : w[1];
+  const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, false);
+  const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(lo, 1.0f, true);
+  const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, false);
+  const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(hi, 1.0f, true);
+  x[0] = a[0]; x[1] = a[1]; x[2] = b[0]; x[3] = b[1];
+  x[4] = c[0]; x[5] = c[1]; x[6] = d[0]; x[7] = d[1];
+}
+
 // The values of x in a lane and in the lane 16 (or 32) away, from gfx950's
 // row exchanges on two copies of x. v_permlane16_swap swaps the odd 16-lane rows
 // of its first operand with the even rows of its second, v_permlane32_swap
@@ -785,22 +797,47 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE, S
           kr[1][j] = read_piece(1, j);
           kr[1][j + kHalf] = read_piece(1, j + kHalf);
         }
-        v8 lo0 = k_operand(kr, 0, j), hi0 = k_operand(kr, 0, j + kHalf);
-        v8 lo1 = k_operand(kr, 1, j), hi1 = k_operand(kr, 1, j + kHalf);
+        v8 lo0, hi0, lo1, hi1;
+        if constexpr (KV8) {
+          // E4M3 codes straight to fp32 (two per exact conversion), turned,
+          // then rounded once to the operand type
+          float fl0[8], fh0[8], fl1[8], fh1[8];
+          e4m3_f32x8(kr[0][j >> 1], (j & 1) != 0, fl0);
+          e4m3_f32x8(kr[0][(j + kHalf) >> 1], ((j + kHalf) & 1) != 0, fh0);
+          e4m3_f32x8(kr[1][j >> 1], (j & 1) != 0, fl1);
+          e4m3_f32x8(kr[1][(j + kHalf) >> 1], ((j + kHalf) & 1) != 0, fh1);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = qk_hd<KV8>(j, g) + e;
-          float c0, s0;
-          rope_cos_sin(tok, s_rope[d], c0, s0);
-          const f32x2 r4 = s_rope4[d];
-          const float c1 = c0 * r4[0] - s0 * r4[1], s1 = s0 * r4[0] + c0 * r4[1];
-          float l = (float)lo0[e], h = (float)hi0[e];
-          lo0[e] = (typename O::et)(l * c0 - h * s0);
-          hi0[e] = (typename O::et)(h * c0 + l * s0);
-          l = (float)lo1[e];
-          h = (float)hi1[e];
-          lo1[e] = (typename O::et)(l * c1 - h * s1);
-          hi1[e] = (typename O::et)(h * c1 + l * s1);
+          for (int e = 0; e < 8; ++e) {
+            const int d = qk_hd<KV8>(j, g) + e;
+            float c0, s0;
+            rope_cos_sin(tok, s_rope[d], c0, s0);
+            const f32x2 r4 = s_rope4[d];
+            const float c1 = c0 * r4[0] - s0 * r4[1], s1 = s0 * r4[0] + c0 * r4[1];
+            lo0[e] = (typename O::et)(fl0[e] * c0 - fh0[e] * s0);
+            hi0[e] = (typename O::et)(fh0[e] * c0 + fl0[e] * s0);
+            lo1[e] = (typename O::et)(fl1[e] * c1 - fh1[e] * s1);
+            hi1[e] = (typename O::et)(fh1[e] * c1 + fl1[e] * s1);
+          }
+        } else {
+          lo0 = k_operand(kr, 0, j);
+          hi0 = k_operand(kr, 0, j + kHalf);
+          lo1 = k_operand(kr, 1, j);
+          hi1 = k_operand(kr, 1, j + kHalf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int d = qk_hd<KV8>(j, g) + e;
+            float c0, s0;
+            rope_cos_sin(tok, s_rope[d], c0, s0);
+            const f32x2 r4 = s_rope4[d];
+            const float c1 = c0 * r4[0] - s0 * r4[1], s1 = s0 * r4[0] + c0 * r4[1];
+            float l = (float)lo0[e], h = (float)hi0[e];
+            lo0[e] = (typename O::et)(l * c0 - h * s0);
+            hi0[e] = (typename O::et)(h * c0 + l * s0);
+            l = (float)lo1[e];
+            h = (float)hi1[e];
+            lo1[e] = (typename O::et)(l * c1 - h * s1);
+            hi1[e] = (typename O::et)(h * c1 + l * s1);
+          }
         }
         sc[0] = O::mfma(lo0, bq[j], sc[0]);
         sc[0] = O::mfma(hi0, bq[j + kHalf], sc[0]);
