@@ -476,13 +476,46 @@ class BatchDecodeWithPagedKVCacheWrapper:
 
     ``float_workspace_buffer`` is a uint8 device tensor used for split-KV
     partial states; it is grown (reallocated) if a plan needs more.
+
+    The constructor takes the page's arguments. With ``use_cuda_graph`` the
+    page table lives in the three ``paged_kv_*_buffer`` tensors (all
+    required) and the wrapper behaves as
+    CUDAGraphBatchDecodeWithPagedKVCacheWrapper: a run captured in a HIP
+    graph follows every later plan() of the same batch size and parameters,
+    and the workspace is not grown. ``use_tensor_cores`` changes nothing
+    (q.K and P.V run on MFMA at every group size); ``backend`` takes "auto"
+    only (one gfx950 implementation) and ``jit_args`` None (the kernels are
+    built ahead of time).
     """
 
     def __init__(self, float_workspace_buffer: torch.Tensor,
-                 kv_layout: str = "NHD"):
+                 kv_layout: str = "NHD", use_cuda_graph: bool = False,
+                 use_tensor_cores: bool = False,
+                 paged_kv_indptr_buffer: Optional[torch.Tensor] = None,
+                 paged_kv_indices_buffer: Optional[torch.Tensor] = None,
+                 paged_kv_last_page_len_buffer: Optional[torch.Tensor] = None,
+                 backend: str = "auto", jit_args=None):
+        if backend != "auto":
+            raise PkdError(PKD_EUNSUPPORTED, f"backend {backend!r}: only 'auto' "
+                           "(the gfx950 kernels of this library)")
+        if jit_args is not None:
+            raise PkdError(PKD_EUNSUPPORTED, "jit_args: the kernels are built "
+                           "ahead of time")
         self._ws = float_workspace_buffer
         self._layout = kv_layout
         self._plan: Optional[PagedDecodePlan] = None
+        self._graph: Optional[CUDAGraphBatchDecodeWithPagedKVCacheWrapper] = None
+        if use_cuda_graph:
+            for name, t in (("paged_kv_indptr_buffer", paged_kv_indptr_buffer),
+                            ("paged_kv_indices_buffer", paged_kv_indices_buffer),
+                            ("paged_kv_last_page_len_buffer",
+                             paged_kv_last_page_len_buffer)):
+                if t is None:
+                    raise PkdError(PKD_EINVAL, f"use_cuda_graph needs {name}")
+            self._graph = CUDAGraphBatchDecodeWithPagedKVCacheWrapper(
+                float_workspace_buffer, paged_kv_indptr_buffer,
+                paged_kv_indices_buffer, paged_kv_last_page_len_buffer,
+                kv_layout, use_tensor_cores)
 
     def reset_workspace_buffer(self, float_workspace_buffer: torch.Tensor,
                                int_workspace_buffer=None) -> None:
@@ -499,6 +532,19 @@ class BatchDecodeWithPagedKVCacheWrapper:
         """plan() of the page. With ``block_tables`` [B, max_blocks] and
         ``seq_lens`` [B] the page table is a block table; indptr, indices and
         last_page_len are then None."""
+        if self._graph is not None:
+            if block_tables is not None or seq_lens is not None:
+                raise PkdError(PKD_EINVAL, "use_cuda_graph keeps a CSR page "
+                               "table in its buffers; block_tables is not "
+                               "taken there")
+            self._graph.plan(indptr, indices, last_page_len, num_qo_heads,
+                             num_kv_heads, head_dim, page_size, pos_encoding_mode,
+                             window_left, logits_soft_cap, q_data_type,
+                             kv_data_type, o_data_type, data_type, sm_scale,
+                             rope_scale, rope_theta, non_blocking,
+                             fixed_split_size, disable_split_kv, q_len_per_req)
+            self._plan = self._graph._plan
+            return
         if data_type is not None:
             q_data_type = data_type
             kv_data_type = kv_data_type or data_type
@@ -519,13 +565,18 @@ class BatchDecodeWithPagedKVCacheWrapper:
 
     def run(self, q, paged_kv_cache, q_scale=None, k_scale=None, v_scale=None,
             out=None, lse=None, return_lse=False, q_len_per_req=None,
-            sinks=None):
+            sinks=None, enable_pdl=None):
+        """run() of the page (``enable_pdl``, a launch feature of other
+        GPUs, changes nothing here)."""
         if self._plan is None:
             raise PkdError(PKD_EINVAL, "run() before plan()")
         planned = max(1, self._plan.params.q_len_per_req)
         if q_len_per_req is not None and int(q_len_per_req) != planned:
             raise PkdError(PKD_EINVAL, f"q_len_per_req {q_len_per_req} differs "
                            f"from the plan's {planned}")
+        if self._graph is not None:
+            return self._graph.run(q, paged_kv_cache, q_scale, k_scale, v_scale,
+                                   out, lse, return_lse, sinks=sinks)
         ws = self._ws if self._plan.workspace_bytes > 0 else None
         return self._plan.run(q, paged_kv_cache, q_scale, k_scale, v_scale,
                               out, lse, return_lse, ws, sinks=sinks)
@@ -615,9 +666,14 @@ class CUDAGraphBatchDecodeWithPagedKVCacheWrapper:
                            f"< {need} needed by the graph plan's capacity")
 
     def run(self, q, paged_kv_cache, q_scale=None, k_scale=None, v_scale=None,
-            out=None, lse=None, return_lse=False, sinks=None):
+            out=None, lse=None, return_lse=False, sinks=None, enable_pdl=None,
+            q_len_per_req=None):
         if self._plan is None:
             raise PkdError(PKD_EINVAL, "run() before plan()")
+        planned = max(1, self._plan.params.q_len_per_req)
+        if q_len_per_req is not None and int(q_len_per_req) != planned:
+            raise PkdError(PKD_EINVAL, f"q_len_per_req {q_len_per_req} differs "
+                           f"from the plan's {planned}")
         ws = self._ws if self._plan.workspace_bytes > 0 else None
         return self._plan.run(q, paged_kv_cache, q_scale, k_scale, v_scale,
                               out, lse, return_lse, ws, sinks=sinks)

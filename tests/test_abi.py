@@ -416,3 +416,25 @@ def test_temporaries_are_kept_for_a_run_on_another_stream(monkeypatch):
         assert all(t.recorded == expect for t in ts), (stream, ts[0].recorded)
     # nothing allocated: nothing to record, and the stream is not looked up
     pkd._keep_for_stream([], 22)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(backend="fa2"), pkd.PKD_EUNSUPPORTED, "backend 'fa2'"),
+    (dict(jit_args=["x"]), pkd.PKD_EUNSUPPORTED, "jit_args"),
+    (dict(use_cuda_graph=True), pkd.PKD_EINVAL, "paged_kv_indptr_buffer"),
+])
+def test_wrapper_constructor_arguments(kw, status, needle):
+    # the page's constructor arguments are taken; those this library cannot
+    # honour fail with the argument's name (no GPU needed to get there)
+    import torch
+    with pytest.raises(pkd.PkdError) as e:
+        pkd.BatchDecodeWithPagedKVCacheWrapper(torch.empty(16, dtype=torch.uint8), **kw)
+    assert e.value.status == status and needle in str(e.value)
+
+
+def test_wrapper_takes_use_tensor_cores():
+    import torch
+    w = pkd.BatchDecodeWithPagedKVCacheWrapper(torch.empty(16, dtype=torch.uint8),
+                                               "HND", use_tensor_cores=True)
+    with pytest.raises(pkd.PkdError, match="run\\(\\) before plan\\(\\)"):
+        w.run(None, None)

@@ -124,3 +124,48 @@ def test_graph_plan_rejects_what_it_cannot_hold():
     plain = plan_for(w, case)
     with pytest.raises(pkd.PkdError):
         pkd._check(pkd.lib().pkd_plan_update(plain._handle, None, None, None))
+
+
+def test_decode_wrapper_with_use_cuda_graph():
+    """The page's BatchDecodeWithPagedKVCacheWrapper(use_cuda_graph=True, with
+    the three page-table buffers): a run captured once follows each new
+    plan(), bit for bit equal to the plain wrapper's eager run of that plan."""
+    w = wl.small_workload(seed=89, batch=5, num_qo_heads=16, num_kv_heads=4, head_dim=128,
+                          q_dtype="f16", kv_dtype="f16", o_dtype="f16", layout="NHD",
+                          pages="perm_pool", pool_pages=POOL)
+    say(w)
+    pool = wl.make_pool(w, POOL, "cuda")
+    dev = "cuda"
+    wrapper = pkd.BatchDecodeWithPagedKVCacheWrapper(
+        torch.empty(64 << 20, dtype=torch.uint8, device=dev), "NHD", use_cuda_graph=True,
+        use_tensor_cores=True,
+        paged_kv_indptr_buffer=torch.empty(w.batch + 1, dtype=torch.int32, device=dev),
+        paged_kv_indices_buffer=torch.empty(MAX_PAGES, dtype=torch.int32, device=dev),
+        paged_kv_last_page_len_buffer=torch.empty(w.batch, dtype=torch.int32, device=dev))
+    plain = pkd.BatchDecodeWithPagedKVCacheWrapper(
+        torch.empty(64 << 20, dtype=torch.uint8, device=dev), "NHD")
+    cases = tables(w, [5, 6, 7])
+    q_static = torch.empty((w.batch, 16, 128), dtype=torch.float16, device=dev)
+    o_static = torch.empty_like(q_static)
+    pt0, q0 = cases[0]
+    args = (16, 4, 128, 16)
+    wrapper.plan(pt0.indptr, torch.from_numpy(pt0.indices).to(dev), pt0.last_page_len, *args)
+    q_static.copy_(q0)
+    wrapper.run(q_static, pool, out=o_static, enable_pdl=False)   # warm-up, eager
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wrapper.run(q_static, pool, out=o_static)
+    torch.cuda.synchronize()
+    for k, (pt, q) in enumerate(cases):
+        say("page table", k, "pages", int(pt.indptr[-1]))
+        idx = torch.from_numpy(pt.indices).to(dev)
+        wrapper.plan(pt.indptr, idx, pt.last_page_len, *args)
+        q_static.copy_(q)
+        o_static.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        plain.plan(pt.indptr, idx, pt.last_page_len, *args)
+        o_ref = plain.run(q, pool)
+        torch.cuda.synchronize()
+        assert torch.equal(o_static, o_ref), k
