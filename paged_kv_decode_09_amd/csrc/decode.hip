@@ -273,9 +273,6 @@ struct Geo {
   static constexpr int kPieces = kRowBytes / 64;
   static constexpr int kQkMfma = HD / 32;   // MFMAs per 16-token tile
   static constexpr int kPvMfma = HD / 16;   // MFMAs per 32-token step
-  // Steps of K/V rows held in registers: the next step's loads are issued
-  // before the current step is computed.
-  static constexpr int kStages = 2;
   // LDS row pitch of the K and V copies; the pad staggers rows across banks.
   static constexpr int kVPitch = kRowBytes + (KV8 ? 16 : 32);
   static constexpr int kVBytes = kStepTokens * kVPitch;
