@@ -271,18 +271,24 @@ def test_empty_batch_runs_nothing():
     assert o.shape == (0, 8, 128)
 
 
-@pytest.mark.parametrize("hd,kv", [(64, "f16"), (64, "e4m3"), (128, "bf16"), (128, "e4m3"), (256, "bf16")])
-def test_host_planning_matches_the_device_occupancy(hd, kv):
+@pytest.mark.parametrize("hd,kv,pos", [(64, "f16", "NONE"), (64, "e4m3", "NONE"),
+                                        (128, "bf16", "NONE"), (128, "e4m3", "NONE"),
+                                        (256, "bf16", "NONE"), (64, "bf16", "ROPE_LLAMA"),
+                                        (128, "bf16", "ROPE_LLAMA"), (128, "e4m3", "ROPE_LLAMA"),
+                                        (256, "f16", "ROPE_LLAMA")])
+def test_host_planning_matches_the_device_occupancy(hd, kv, pos):
     """pkd_plan_query (no GPU) must plan the same workgroups as
-    pkd_plan_create, whose slot count comes from the HIP runtime."""
+    pkd_plan_create, whose slot count comes from the HIP runtime (with RoPE
+    at head_dim 128: two workgroups of the one-buffer kernel per compute
+    unit, which their LDS must allow)."""
     import paged_kv_decode_09_amd as pkd
-    say("occupancy", hd, kv)
+    say("occupancy", hd, kv, pos)
     qd = "bf16" if kv == "e4m3" else kv
     rng = np.random.default_rng(1)
     lens = rng.integers(100, 20000, 300)
     pt = wl.page_table_for(lens, 16, "perm_used", rng)
     kw = dict(num_qo_heads=32, num_kv_heads=8, head_dim=hd, page_size=16,
-              q_data_type=qd, kv_data_type=kv)
+              q_data_type=qd, kv_data_type=kv, pos_encoding_mode=pos)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     info, items = pkd.plan_query(pt.indptr, pt.last_page_len, cus, **kw)
     plan = pkd.PagedDecodePlan(pt.indptr, torch.from_numpy(pt.indices).cuda(),
