@@ -1164,6 +1164,8 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE, S
             if (k == 0) {
               load_next();
               if (w0 == 0 && claimed) {
+                // the claim of cur returned with its first step (as in the
+                // two-buffer loop below): stolen means no outputs
                 if (threadIdx.x == 0) s_drop = (claim & kStolen) != 0;
                 lds_barrier();
                 drop = __builtin_amdgcn_readfirstlane(s_drop) != 0;
@@ -1177,6 +1179,9 @@ __global__ __launch_bounds__(kWaves * 64, decode_waves_per_simd(HD, KV8, ROPE, S
             if (k + 1 < n1) {
               issue(W, s + kWaves, A);
             } else {
+              // the last step: thread 0 claims nxt and takes the ticket (in
+              // range only after the last window, as below), then the next
+              // unit's first step, or a clamped padding step, is issued
               const bool hand = w1 == nsteps && nxt < a.num_items;
               const uint32_t coff = hand && nxt < a.steal_limit && threadIdx.x == 0
                                         ? (uint32_t)(2 * blockIdx.x + (par ^ 1)) * 4u
