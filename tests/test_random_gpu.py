@@ -19,7 +19,7 @@ from helpers import (LSE_TOL, o_bounds, plan_for, rope_lse_bounds, rope_o_bounds
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 64
+N_CASES = 256
 
 
 def say(*a):
